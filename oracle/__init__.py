@@ -1,0 +1,29 @@
+"""fp64 CPU oracle for single-pass attention and the two-pass row softmax.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports this package:
+only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may call it.  It shares no code with the HIP library.
+
+Contents
+--------
+attention        the plain definition O = softmax(mask(Q K^T * scale)) V with
+                 GQA and a top-left causal mask, materialising the score matrix
+                 (page "从零开始写Qwen3（五-其一）使用Triton实现自注意力",
+                 section 自注意力原理; page "softmax_attention", section 实现思路).
+attention_rows   the same definition for a chosen set of query rows of one head.
+softmax_rows     the stable row softmax (page "Softmax 算子的实现与优化", the
+                 max-shifted definition; page "Puzzle 8: Long Softmax", its spec).
+recurrence       a blockwise model of the online recurrence (running max, running
+                 denominator, unnormalised accumulator) used to check page-fixed
+                 facts against the definition; it is not the oracle.
+brute            pure-Python loops over tiny inputs.
+
+Every function is pinned by ``tests/test_oracle_pins.py`` to values, closed
+forms and invariants the pages and the mathematics fix.  No function here is
+"parity unpinned".
+"""
+from .attention import attention, attention_rows, bf16_bits_to_f64
+from .softmax import softmax_rows
+from . import recurrence, brute
+
+__all__ = ["attention", "attention_rows", "softmax_rows", "bf16_bits_to_f64", "recurrence", "brute"]
