@@ -1,0 +1,293 @@
+#!/usr/bin/env python3
+"""Benchmark of the online-softmax attention path on one MI355X.
+
+One step = one ``osx_attn_fwd`` call on the GQA causal prefill workload (bf16,
+B=2, Hq=32, Hkv=8, S=4096, d=128): every step of the single-pass attention
+hot path runs in it.  The headline ``value`` is its causal-adjusted TFLOP/s
+(4*B*Hq*S*S*d / 2 flops per call).  The other hot-path calls are timed in the
+same run and reported under ``also``: GQA decode (GB/s over K/V), the long-row
+softmax (GB/s, 2 reads + 1 write), the fp32 4096^2 attention (TFLOP/s) and the
+two small latency cases (microseconds).
+
+Inputs are seeded synthetic tensors (``synth``), generated on the host and
+copied to HBM before timing.  Kernel durations come from HIP events recorded
+on the stream the kernels run on, around every call in the timed region.
+
+``--gpus N`` with N > 1 exits: this build runs on one GPU.
+Prints one JSON line on stdout.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 MFMA / vector
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "attn fwd TFLOP/s (causal-adjusted) & softmax/decode GB/s, % of MI355X peak"
+KERNEL_SOURCES = {
+    "prefill_bf16_kernel": "online_softmax_02_amd/csrc/attn_prefill_bf16.hip",
+    "decode_bf16_kernel": "online_softmax_02_amd/csrc/attn_decode_bf16.hip",
+    "softmax_split": "online_softmax_02_amd/csrc/softmax_rows.hip",
+    "prefill_f32_kernel": "online_softmax_02_amd/csrc/attn_prefill_f32.hip",
+}
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--only", default="all", choices=["all", "prefill", "decode", "softmax", "f32", "small", "copy"],
+                   help="time one workload only (for profiler runs)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle timing sample")
+    return p.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def sha_of(rel):
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_for(kernel: str):
+    """HBM bytes per launch from committed PMC counters, or None if absent or stale."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{kernel}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256") != sha_of(KERNEL_SOURCES[kernel]):
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def timed(torch, fn, steps, warmup):
+    """Warm up, then time `steps` calls; returns (wall seconds, per-call ms list)."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        fn(warmup + i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, [a.elapsed_time(b) for a, b in ev]
+
+
+def to_dev(a):
+    """numpy (fp32, or bf16 bit patterns as uint16) -> CUDA tensor."""
+    import numpy as np
+    import torch
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def attn_tensors(torch, w):
+    import synth
+    t0 = time.perf_counter()
+    t = synth.attn_inputs(w)
+    log(f"[bench] generated {w.name} in {time.perf_counter() - t0:.1f}s")
+    return t, to_dev(t["q"]), to_dev(t["k"]), to_dev(t["v"])
+
+
+def roofline(bound, achieved, peak, unit, traffic):
+    return {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic}
+
+
+def bench_prefill(torch, osx, args):
+    import synth
+    w = synth.WORKLOADS["gqa_prefill_bf16"]
+    t, q, k, v = attn_tensors(torch, w)
+    out = torch.empty_like(q)
+    wall, per = timed(torch, lambda i: osx.attn_fwd(q, k, v, causal=True, out=out), args.steps, args.warmup)
+    kern_ms = sum(per) / len(per)
+    tflops = w.flops() / (kern_ms * 1e-3) / 1e12
+    res = {"wall_s": wall, "ms_per_step": wall / args.steps * 1e3, "kernel_ms": kern_ms, "tflops": tflops,
+           "roofline": roofline("mfma", tflops, PEAK_BF16_TFLOPS, "TFLOP/s", traffic_for("prefill_bf16_kernel"))}
+    return res, t, w
+
+
+def bench_decode(torch, osx, args):
+    import synth
+    w = synth.WORKLOADS["gqa_decode_bf16"]
+    _, q, k, v = attn_tensors(torch, w)
+    out = torch.empty_like(q)
+    ws = torch.empty(osx.attn_fwd_workspace(osx.OSX_BF16, w.batch, w.heads_q, w.heads_kv, 1, w.seq_k, w.head_dim),
+                     dtype=torch.uint8, device="cuda")
+    wall, per = timed(torch, lambda i: osx.attn_fwd(q, k, v, out=out, workspace=ws), args.steps, args.warmup)
+    ms = sum(per) / len(per)
+    gbs = w.bytes() / (ms * 1e-3) / 1e9
+    return {"workload": w.name, "unit": "GB/s", "value": round(gbs, 1), "call_us": round(ms * 1e3, 2),
+            "bytes_per_call": w.bytes(),
+            "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", traffic_for("decode_bf16_kernel"))}
+
+
+def bench_softmax(torch, osx, args):
+    import synth
+    w = synth.WORKLOADS["softmax_1x16m"]
+    x = to_dev(synth.softmax_inputs(w))
+    # 5 input/output pairs (640 MiB) rotate so no call finds its data in the 256 MB MALL.
+    xs = [x.clone() for _ in range(5)]
+    ys = [torch.empty_like(x) for _ in range(5)]
+    ws = torch.empty(osx.softmax_rows_workspace(w.rows, w.cols), dtype=torch.uint8, device="cuda")
+    wall, per = timed(torch, lambda i: osx.softmax_rows(xs[i % 5], out=ys[i % 5], workspace=ws), args.steps,
+                      args.warmup)
+    ms = sum(per) / len(per)
+    gbs = w.bytes() / (ms * 1e-3) / 1e9
+    return {"workload": w.name, "unit": "GB/s", "value": round(gbs, 1), "call_us": round(ms * 1e3, 2),
+            "bytes_per_call": w.bytes(),
+            "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", traffic_for("softmax_split"))}
+
+
+def bench_f32(torch, osx, args):
+    import synth
+    w = synth.WORKLOADS["attn_f32_4k_d128"]
+    _, q, k, v = attn_tensors(torch, w)
+    out = torch.empty_like(q)
+    wall, per = timed(torch, lambda i: osx.attn_fwd(q, k, v, out=out), args.steps, args.warmup)
+    ms = sum(per) / len(per)
+    tf = w.flops() / (ms * 1e-3) / 1e12
+    return {"workload": w.name, "unit": "TFLOP/s", "value": round(tf, 2), "call_us": round(ms * 1e3, 2),
+            "roofline": roofline("mfma", tf, PEAK_F32_TFLOPS, "TFLOP/s", traffic_for("prefill_f32_kernel"))}
+
+
+def bench_small(torch, osx, args):
+    import synth
+    res = {}
+    w = synth.WORKLOADS["attn_f32_m64_n100_d48"]
+    _, q, k, v = attn_tensors(torch, w)
+    out = torch.empty_like(q)
+    _, per = timed(torch, lambda i: osx.attn_fwd(q, k, v, out=out), args.steps, args.warmup)
+    res[w.name] = {"unit": "us", "value": round(1e3 * sum(per) / len(per), 2),
+                   "note": "launch-latency bound; roofline fraction not meaningful"}
+    w = synth.WORKLOADS["softmax_4x200"]
+    x = to_dev(synth.softmax_inputs(w))
+    y = torch.empty_like(x)
+    _, per = timed(torch, lambda i: osx.softmax_rows(x, out=y), args.steps, args.warmup)
+    res[w.name] = {"unit": "us", "value": round(1e3 * sum(per) / len(per), 2),
+                   "note": "launch-latency bound; roofline fraction not meaningful"}
+    return res
+
+
+def bench_copy(torch, args):
+    """A plain device copy of known size (256 MiB), to calibrate the HBM byte counters."""
+    n = 64 << 20
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    timed(torch, lambda i: b.copy_(a), args.steps, args.warmup)
+    return {"bytes_read": 4 * n, "bytes_written": 4 * n}
+
+
+def cpu_baseline(t, w, seconds):
+    """The fp64 oracle on whole (batch, head) slices of the prefill workload, timed on the host."""
+    import numpy as np
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    G = w.groups
+    heads = [(b, h) for b in range(w.batch) for h in range(w.heads_q)]
+    order = np.random.default_rng(0).permutation(len(heads))
+    rows = np.arange(w.seq_q)
+    done = 0
+    t0 = time.perf_counter()
+    for idx in order:
+        b, h = heads[idx]
+        oracle.attention_rows(t["q"][b, h], t["k"][b, h // G], t["v"][b, h // G], rows, causal=True, seq_q=w.seq_q)
+        done += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    flops = done * 4.0 * w.seq_q * w.seq_k * w.head_dim * 0.5
+    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {len(heads)} (batch, query head) slices of {w.name}, all {w.seq_q} rows each, "
+                      f"{el:.1f}s; causal-adjusted flop count (the oracle computes the dense score matrix)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} requested; this build runs on exactly one GPU "
+              "(no collectives or sharding). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import online_softmax_02_amd as osx
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    log(f"[bench] device {torch.cuda.get_device_name(0)}; library {osx.LIB_PATH}")
+
+    if args.only == "copy":
+        print(json.dumps({"copy": bench_copy(torch, args)}))
+        return
+    also = {}
+    if args.only in ("decode",):
+        also["gqa_decode_bf16"] = bench_decode(torch, osx, args)
+        print(json.dumps({"also": also}))
+        return
+    if args.only in ("softmax",):
+        also["softmax_1x16m"] = bench_softmax(torch, osx, args)
+        print(json.dumps({"also": also}))
+        return
+    if args.only in ("f32",):
+        also["attn_f32_4k_d128"] = bench_f32(torch, osx, args)
+        print(json.dumps({"also": also}))
+        return
+    if args.only in ("small",):
+        print(json.dumps({"also": bench_small(torch, osx, args)}))
+        return
+
+    head, t, w = bench_prefill(torch, osx, args)
+    log(f"[bench] prefill {head['tflops']:.1f} TFLOP/s ({head['kernel_ms']:.3f} ms per call)")
+    if args.only == "all":
+        also["gqa_decode_bf16"] = bench_decode(torch, osx, args)
+        log(f"[bench] decode {also['gqa_decode_bf16']['value']} GB/s")
+        also["softmax_1x16m"] = bench_softmax(torch, osx, args)
+        log(f"[bench] softmax {also['softmax_1x16m']['value']} GB/s")
+        also["attn_f32_4k_d128"] = bench_f32(torch, osx, args)
+        log(f"[bench] fp32 attention {also['attn_f32_4k_d128']['value']} TFLOP/s")
+        also.update(bench_small(torch, osx, args))
+    cpu = None
+    if not args.no_cpu_baseline and args.only == "all":
+        log("[bench] timing the oracle on the host")
+        cpu = cpu_baseline(t, w, args.cpu_seconds)
+    rec = {
+        "metric": METRIC,
+        "value": round(head["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), rounded to bf16)",
+        "config": {"workload": w.name, "batch": w.batch, "heads_q": w.heads_q, "heads_kv": w.heads_kv,
+                   "seq_q": w.seq_q, "seq_k": w.seq_k, "head_dim": w.head_dim, "causal": w.causal,
+                   "parallelism": "none (one GPU)"},
+        "kernel_ms": round(head["kernel_ms"], 4),
+        "roofline": head["roofline"],
+        "cpu_baseline": cpu,
+        "also": also,
+    }
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

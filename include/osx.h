@@ -1,0 +1,138 @@
+/*
+ * osx.h -- C ABI of the MI355X (gfx950) online-softmax attention library.
+ *
+ * Two operations, both computed by hand-written HIP kernels:
+ *
+ *   osx_attn_fwd      O = softmax(mask(Q K^T * scale)) V, one pass over K/V
+ *                     with a running max, denominator and unnormalised
+ *                     accumulator (page "softmax_attention", section 实现思路;
+ *                     GQA and causal masking as in page
+ *                     "从零开始写Qwen3（五-其一）使用Triton实现自注意力",
+ *                     sections 自注意力原理 and GQA).
+ *   osx_softmax_rows  y = softmax(x) along each row, two passes: an online
+ *                     (max, sum) pass, then a normalise pass (page
+ *                     "Softmax 算子的实现与优化", section Online Softmax;
+ *                     page "Puzzle 8: Long Softmax").
+ *
+ * Conventions for every entry point:
+ *   - Pointers q, k, v, o, x, y, workspace are DEVICE pointers owned by the
+ *     caller; the library allocates no device memory, keeps no pointer after
+ *     it returns and has no global mutable state besides a thread-local error
+ *     message.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     asynchronously on it; nothing synchronises the device.  Buffers must stay
+ *     alive until that work has finished.
+ *   - Arguments are checked on the host before anything is launched.  On error
+ *     nothing is launched and a negative status is returned; osx_last_error()
+ *     then describes the failure.  A call with no work (an empty batch, zero
+ *     query rows, zero rows or columns) returns OSX_OK and launches nothing.
+ */
+#ifndef OSX_H
+#define OSX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define OSX_OK 0
+#define OSX_EINVAL (-1)      /* bad argument: null pointer, negative size, Hq % Hkv != 0, empty softmax, overlap */
+#define OSX_EUNSUPPORTED (-2) /* valid request outside what the kernels implement (head_dim, causal with Sq != Sk) */
+#define OSX_EHIP (-3)        /* the HIP runtime reported an error at launch */
+#define OSX_EWORKSPACE (-4)  /* workspace missing or smaller than the size the query returns */
+
+/* Element types of q, k, v, o.  Accumulation is fp32 in both. */
+#define OSX_F32 0
+#define OSX_BF16 1
+
+/* Kernel families chosen by the planner. */
+#define OSX_KERNEL_NONE 0          /* no work */
+#define OSX_KERNEL_PREFILL_F32 1   /* fp32 MFMA tiles, any seq_q */
+#define OSX_KERNEL_PREFILL_BF16 2  /* bf16 MFMA tiles, any seq_q */
+#define OSX_KERNEL_DECODE_BF16 3   /* bf16, seq_q == 1: K/V split across workgroups + combine */
+#define OSX_KERNEL_SOFTMAX_ROW 4   /* one workgroup per row */
+#define OSX_KERNEL_SOFTMAX_SPLIT 5 /* rows split across workgroups, (m, l) partials merged */
+
+/* What the library will launch for a given problem (filled by the plan calls). */
+typedef struct osx_plan {
+  int kernel;             /* OSX_KERNEL_* */
+  int threads;            /* threads per workgroup of the main kernel */
+  int block_m;            /* query rows (attention) or elements (softmax) per workgroup */
+  int block_n;            /* keys per LDS block (attention) */
+  int splits;             /* K/V splits per (batch, KV head) (decode) or chunks per row (softmax) */
+  int heads_per_wg;       /* query heads sharing one workgroup (attention) */
+  int64_t grid;           /* workgroups of the main kernel */
+  size_t workspace_bytes; /* bytes of workspace the call needs (0 = none) */
+} osx_plan;
+
+/*
+ * osx_attn_plan -- choose the kernel for an attention problem; no HIP calls.
+ *
+ * Shapes (all tensors contiguous, last dimension stride 1, row-major):
+ *   q, o : [batch, heads_q,  seq_q, head_dim]
+ *   k, v : [batch, heads_kv, seq_k, head_dim]
+ * Query head h reads KV head h / (heads_q / heads_kv) (page
+ * "从零开始写Qwen3（五-其一）使用Triton实现自注意力", section GQA).
+ * causal != 0 keeps key j for query i only when j <= i, and only when
+ * seq_q > 1 (the eager reference of section 自注意力原理 skips the mask for a
+ * single query row); with seq_q > 1 it requires seq_q == seq_k.
+ * Supported head_dim: fp32 any multiple of 4 in [4, 128]; bf16 64 or 128.
+ * Returns OSX_OK, OSX_EINVAL or OSX_EUNSUPPORTED; `out` may be NULL.
+ */
+int osx_attn_plan(int dtype, int batch, int heads_q, int heads_kv, int seq_q, int seq_k, int head_dim, int causal,
+                  osx_plan* out);
+
+/* Workspace bytes osx_attn_fwd needs for this problem (0 for prefill), via *bytes. */
+int osx_attn_fwd_workspace(int dtype, int batch, int heads_q, int heads_kv, int seq_q, int seq_k, int head_dim,
+                           int causal, size_t* bytes);
+
+/*
+ * osx_attn_fwd -- single-pass attention forward.
+ *
+ * q, k, v, o: device pointers in the layouts above, all of element type
+ * `dtype` (OSX_F32 or OSX_BF16); o is written in full.  scale <= 0 selects
+ * 1/sqrt(head_dim) (page "softmax_attention": scores are multiplied by
+ * d^-0.5).  workspace: device buffer of at least the bytes
+ * osx_attn_fwd_workspace reports (may be NULL when that is 0); its contents
+ * on entry do not matter.  o must not overlap q, k, v or the workspace.
+ */
+int osx_attn_fwd(const void* q, const void* k, const void* v, void* o, int dtype, int batch, int heads_q,
+                 int heads_kv, int seq_q, int seq_k, int head_dim, int causal, float scale, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
+/* osx_softmax_rows_plan -- kernel choice for x[rows, cols]; no HIP calls. */
+int osx_softmax_rows_plan(int64_t rows, int64_t cols, osx_plan* out);
+
+/* Workspace bytes osx_softmax_rows needs for x[rows, cols] (0 when one workgroup per row), via *bytes. */
+int osx_softmax_rows_workspace(int64_t rows, int64_t cols, size_t* bytes);
+
+/*
+ * osx_softmax_rows -- y[r, :] = exp(x[r, :] - m_r) / l_r for every row r, with
+ * m_r the row max and l_r = sum_j exp(x[r, j] - m_r), found in one online pass
+ * over x, then a second pass over x writes y (page "Softmax 算子的实现与优化",
+ * section Online Softmax).
+ *
+ * x, y: device fp32 [rows, cols], contiguous.  y == x (in place) is allowed;
+ * any other overlap is OSX_EINVAL.  cols == 0 with rows > 0 is OSX_EINVAL (a
+ * softmax over nothing).  workspace as for osx_attn_fwd.
+ */
+int osx_softmax_rows(const float* x, float* y, int64_t rows, int64_t cols, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* Static text for a status code. */
+const char* osx_status_string(int status);
+
+/* Detail of the last failing call on this thread ("" if none). */
+const char* osx_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int osx_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OSX_H */

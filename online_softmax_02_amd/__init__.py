@@ -1,0 +1,197 @@
+"""Online-softmax attention and row softmax on MI355X (gfx950).
+
+A thin ``ctypes`` binding over ``libosx.so`` (the C ABI in ``include/osx.h``).
+It only marshals arguments: every step of the computation runs in the
+library's HIP kernels.  PyTorch supplies device memory and the current stream.
+
+The library must be built first (``python -m online_softmax_02_amd.build``);
+importing this package without it raises ``ImportError``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libosx.so")
+
+OSX_OK, OSX_EINVAL, OSX_EUNSUPPORTED, OSX_EHIP, OSX_EWORKSPACE = 0, -1, -2, -3, -4
+OSX_F32, OSX_BF16 = 0, 1
+KERNELS = {0: "none", 1: "prefill_f32", 2: "prefill_bf16", 3: "decode_bf16", 4: "softmax_row", 5: "softmax_split"}
+
+_i, _i64, _sz, _vp, _f = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("kernel", _i), ("threads", _i), ("block_m", _i), ("block_n", _i), ("splits", _i),
+                ("heads_per_wg", _i), ("grid", _i64), ("workspace_bytes", _sz)]
+
+    def as_dict(self) -> dict:
+        d = {name: getattr(self, name) for name, _ in self._fields_}
+        d["kernel_name"] = KERNELS.get(self.kernel, "?")
+        return d
+
+
+class OsxError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{status_string(status)}: {detail}")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m online_softmax_02_amd.build` "
+                          "(hipcc for gfx950); there is no fallback implementation")
+    lib = ctypes.CDLL(LIB_PATH)
+    attn_shape = [_i, _i, _i, _i, _i, _i, _i, _i]  # dtype, B, Hq, Hkv, Sq, Sk, D, causal
+    lib.osx_attn_plan.argtypes = attn_shape + [ctypes.POINTER(Plan)]
+    lib.osx_attn_fwd_workspace.argtypes = attn_shape + [ctypes.POINTER(_sz)]
+    lib.osx_attn_fwd.argtypes = [_vp, _vp, _vp, _vp] + attn_shape + [_f, _vp, _sz, _vp]
+    lib.osx_softmax_rows_plan.argtypes = [_i64, _i64, ctypes.POINTER(Plan)]
+    lib.osx_softmax_rows_workspace.argtypes = [_i64, _i64, ctypes.POINTER(_sz)]
+    lib.osx_softmax_rows.argtypes = [_vp, _vp, _i64, _i64, _vp, _sz, _vp]
+    lib.osx_status_string.argtypes = [_i]
+    lib.osx_status_string.restype = ctypes.c_char_p
+    lib.osx_last_error.argtypes = []
+    lib.osx_last_error.restype = ctypes.c_char_p
+    lib.osx_version.argtypes = []
+    for name in ("osx_attn_plan", "osx_attn_fwd_workspace", "osx_attn_fwd", "osx_softmax_rows_plan",
+                 "osx_softmax_rows_workspace", "osx_softmax_rows", "osx_version"):
+        getattr(lib, name).restype = _i
+    return lib
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.osx_status_string(status).decode()
+
+
+def last_error() -> str:
+    return lib.osx_last_error().decode()
+
+
+def version() -> int:
+    return lib.osx_version()
+
+
+def _check(status: int) -> None:
+    if status != OSX_OK:
+        raise OsxError(status, last_error())
+
+
+def attn_plan(dtype: int, batch: int, heads_q: int, heads_kv: int, seq_q: int, seq_k: int, head_dim: int,
+              causal: bool = False) -> dict:
+    """Kernel choice for an attention problem (no GPU needed); raises OsxError on bad arguments."""
+    p = Plan()
+    _check(lib.osx_attn_plan(dtype, batch, heads_q, heads_kv, seq_q, seq_k, head_dim, int(causal), ctypes.byref(p)))
+    return p.as_dict()
+
+
+def attn_fwd_workspace(dtype: int, batch: int, heads_q: int, heads_kv: int, seq_q: int, seq_k: int, head_dim: int,
+                       causal: bool = False) -> int:
+    n = _sz(0)
+    _check(lib.osx_attn_fwd_workspace(dtype, batch, heads_q, heads_kv, seq_q, seq_k, head_dim, int(causal),
+                                      ctypes.byref(n)))
+    return n.value
+
+
+def softmax_rows_plan(rows: int, cols: int) -> dict:
+    p = Plan()
+    _check(lib.osx_softmax_rows_plan(rows, cols, ctypes.byref(p)))
+    return p.as_dict()
+
+
+def softmax_rows_workspace(rows: int, cols: int) -> int:
+    n = _sz(0)
+    _check(lib.osx_softmax_rows_workspace(rows, cols, ctypes.byref(n)))
+    return n.value
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(t, stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return _vp(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return OSX_F32
+    if t.dtype == torch.bfloat16:
+        return OSX_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}: float32 or bfloat16")
+
+
+def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, workspace=None, stream=None):
+    """O = softmax(mask(q k^T * scale)) v on the GPU.
+
+    q: [B, Hq, Sq, D] (or [M, D] for one head), k, v: [B, Hkv, Sk, D] (or
+    [N, D]); contiguous CUDA tensors of one dtype (float32 or bfloat16).
+    Query head h reads KV head h // (Hq // Hkv).  Returns a tensor like q.
+    """
+    torch = _torch()
+    squeeze = q.dim() == 2
+    if squeeze:
+        q, k, v = q[None, None], k[None, None], v[None, None]
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, S, D] (or 2-D [S, D])")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous CUDA tensor")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share one dtype")
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    B, Hq, Sq, D = q.shape
+    Bk, Hkv, Sk, Dk = k.shape
+    if Bk != B or Dk != D:
+        raise ValueError("batch and head_dim of q and k must match")
+    code = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    need = attn_fwd_workspace(code, B, Hq, Hkv, Sq, Sk, D, causal)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.osx_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), code, B, Hq, Hkv, Sq, Sk, D,
+                            int(causal), float(scale) if scale else 0.0, ws_ptr, ws_len, _stream(q, stream)))
+    return out[0, 0] if squeeze else out
+
+
+def softmax_rows(x, out=None, workspace=None, stream=None):
+    """y = softmax(x) along the last dimension of a contiguous float32 CUDA tensor (2-D or 1-D).
+
+    ``out`` may be ``x`` itself (in place).
+    """
+    torch = _torch()
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous float32 CUDA tensor")
+    cols = x.shape[-1] if x.dim() else 1
+    rows = x.numel() // cols if cols else 0
+    if out is None:
+        out = torch.empty_like(x)
+    elif out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like x")
+    need = softmax_rows_workspace(rows, cols)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.osx_softmax_rows(x.data_ptr(), out.data_ptr(), rows, cols, ws_ptr, ws_len, _stream(x, stream)))
+    return out
+
+
+__all__ = ["attn_fwd", "softmax_rows", "attn_plan", "attn_fwd_workspace", "softmax_rows_plan",
+           "softmax_rows_workspace", "status_string", "last_error", "version", "OsxError", "lib", "LIB_PATH",
+           "OSX_F32", "OSX_BF16"]

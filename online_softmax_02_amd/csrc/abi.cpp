@@ -1,0 +1,240 @@
+// C ABI: argument checks, kernel planning and dispatch.  No device memory is
+// allocated here and nothing synchronises the device.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "launch.hpp"
+#include "osx.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return OSX_OK;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Largest of 4, 2, 1 that divides the group size: that many query heads of one
+// KV head share a workgroup; the remaining wavefronts take further row tiles.
+int heads_per_wg(int groups) { return groups % 4 == 0 ? 4 : (groups % 2 == 0 ? 2 : 1); }
+
+int plan_attn(int dtype, int batch, int heads_q, int heads_kv, int seq_q, int seq_k, int head_dim, int causal,
+              osx_plan* p) {
+  std::memset(p, 0, sizeof *p);
+  if (dtype != OSX_F32 && dtype != OSX_BF16) return fail(OSX_EINVAL, "dtype %d is neither OSX_F32 nor OSX_BF16", dtype);
+  if (batch < 0 || heads_q < 0 || heads_kv < 0 || seq_q < 0 || seq_k < 0 || head_dim < 0)
+    return fail(OSX_EINVAL, "negative size (batch=%d heads_q=%d heads_kv=%d seq_q=%d seq_k=%d head_dim=%d)", batch,
+                heads_q, heads_kv, seq_q, seq_k, head_dim);
+  if ((int64_t)batch * heads_q * seq_q == 0) return ok();  // nothing to compute
+  if (heads_kv == 0 || heads_q % heads_kv != 0)
+    return fail(OSX_EINVAL, "heads_q (%d) must be a positive multiple of heads_kv (%d)", heads_q, heads_kv);
+  if (seq_k == 0) return fail(OSX_EINVAL, "seq_k == 0 with seq_q > 0: softmax over no keys");
+  if (head_dim == 0) return fail(OSX_EINVAL, "head_dim == 0");
+  if (dtype == OSX_F32 && (head_dim % 4 != 0 || head_dim > 128))
+    return fail(OSX_EUNSUPPORTED, "fp32 head_dim %d: must be a multiple of 4 and at most 128", head_dim);
+  if (dtype == OSX_BF16 && head_dim != 64 && head_dim != 128)
+    return fail(OSX_EUNSUPPORTED, "bf16 head_dim %d: must be 64 or 128", head_dim);
+  if (causal && seq_q > 1 && seq_q != seq_k)
+    return fail(OSX_EUNSUPPORTED, "causal with seq_q (%d) != seq_k (%d): mask alignment is not defined", seq_q,
+                seq_k);
+  const int groups = heads_q / heads_kv;
+  if (dtype == OSX_BF16 && seq_q == 1 && groups <= osx::kDecodeMaxGroup) {
+    const int64_t units = (int64_t)batch * heads_kv;
+    int64_t splits = cdiv(osx::kDecodeTargetWgs, units);
+    const int64_t max_splits = cdiv(seq_k, osx::kDecodeBlockN * osx::kAttnWaves);
+    if (splits > max_splits) splits = max_splits;
+    if (splits < 1) splits = 1;
+    p->kernel = OSX_KERNEL_DECODE_BF16;
+    p->threads = osx::kAttnThreads;
+    p->block_m = groups;
+    p->block_n = osx::kDecodeBlockN;
+    p->splits = (int)splits;
+    p->heads_per_wg = groups;
+    p->grid = units * splits;
+    p->workspace_bytes = (size_t)(units * splits * groups) * (size_t)(2 + head_dim) * sizeof(float);
+    return ok();
+  }
+  const int hp = heads_per_wg(groups);
+  const int rows_per_wg = osx::kRowsPerWave * (osx::kAttnWaves / hp);
+  p->kernel = dtype == OSX_BF16 ? OSX_KERNEL_PREFILL_BF16 : OSX_KERNEL_PREFILL_F32;
+  p->threads = osx::kAttnThreads;
+  p->block_m = rows_per_wg;
+  p->block_n = dtype == OSX_BF16 ? osx::kBf16BlockN : osx::kF32BlockN;
+  p->splits = 1;
+  p->heads_per_wg = hp;
+  p->grid = (int64_t)batch * heads_kv * (groups / hp) * cdiv(seq_q, rows_per_wg);
+  p->workspace_bytes = 0;
+  if (p->grid > 0x7fffffff) return fail(OSX_EUNSUPPORTED, "problem needs %lld workgroups", (long long)p->grid);
+  return ok();
+}
+
+int plan_softmax(int64_t rows, int64_t cols, osx_plan* p) {
+  std::memset(p, 0, sizeof *p);
+  if (rows < 0 || cols < 0) return fail(OSX_EINVAL, "negative size (rows=%lld cols=%lld)", (long long)rows,
+                                        (long long)cols);
+  if (rows == 0) return ok();
+  if (cols == 0) return fail(OSX_EINVAL, "cols == 0 with rows > 0: softmax over nothing");
+  p->threads = osx::kSoftmaxThreads;
+  if (cols <= osx::kSoftmaxRowMax) {
+    p->kernel = OSX_KERNEL_SOFTMAX_ROW;
+    p->block_m = (int)cols;
+    p->splits = 1;
+    p->grid = rows;
+    p->workspace_bytes = 0;
+  } else {
+    const int64_t splits = cdiv(cols, osx::kSoftmaxChunk);
+    p->kernel = OSX_KERNEL_SOFTMAX_SPLIT;
+    p->block_m = (int)osx::kSoftmaxChunk;
+    p->splits = (int)splits;
+    p->grid = rows * splits;
+    p->workspace_bytes = (size_t)(rows * splits) * 2 * sizeof(float);
+  }
+  if (p->grid > 0x7fffffff) return fail(OSX_EUNSUPPORTED, "problem needs %lld workgroups", (long long)p->grid);
+  return ok();
+}
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const char* pa = (const char*)a;
+  const char* pb = (const char*)b;
+  return pa < pb + nb && pb < pa + na;
+}
+
+}  // namespace
+
+extern "C" {
+
+int osx_attn_plan(int dtype, int batch, int heads_q, int heads_kv, int seq_q, int seq_k, int head_dim, int causal,
+                  osx_plan* out) {
+  osx_plan p;
+  int st = plan_attn(dtype, batch, heads_q, heads_kv, seq_q, seq_k, head_dim, causal, &p);
+  if (out) *out = p;
+  return st;
+}
+
+int osx_attn_fwd_workspace(int dtype, int batch, int heads_q, int heads_kv, int seq_q, int seq_k, int head_dim,
+                           int causal, size_t* bytes) {
+  osx_plan p;
+  int st = plan_attn(dtype, batch, heads_q, heads_kv, seq_q, seq_k, head_dim, causal, &p);
+  if (bytes) *bytes = st == OSX_OK ? p.workspace_bytes : 0;
+  return st;
+}
+
+int osx_attn_fwd(const void* q, const void* k, const void* v, void* o, int dtype, int batch, int heads_q,
+                 int heads_kv, int seq_q, int seq_k, int head_dim, int causal, float scale, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  osx_plan p;
+  int st = plan_attn(dtype, batch, heads_q, heads_kv, seq_q, seq_k, head_dim, causal, &p);
+  if (st != OSX_OK) return st;
+  if (p.kernel == OSX_KERNEL_NONE) return ok();
+  if (!q || !k || !v || !o) return fail(OSX_EINVAL, "null q, k, v or o pointer");
+  if (p.workspace_bytes > 0 && (!workspace || workspace_bytes < p.workspace_bytes))
+    return fail(OSX_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : (size_t)0,
+                p.workspace_bytes);
+  if (!(scale > 0.0f) || !std::isfinite(scale)) scale = 1.0f / std::sqrt((float)head_dim);
+  const size_t es = dtype == OSX_BF16 ? 2 : 4;
+  const size_t nq = (size_t)batch * heads_q * seq_q * head_dim * es;
+  const size_t nkv = (size_t)batch * heads_kv * seq_k * head_dim * es;
+  if (overlap(o, nq, q, nq) || overlap(o, nq, k, nkv) || overlap(o, nq, v, nkv) ||
+      (p.workspace_bytes && overlap(o, nq, workspace, p.workspace_bytes)))
+    return fail(OSX_EINVAL, "output overlaps an input or the workspace");
+  osx::AttnArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.batch = batch;
+  a.heads_q = heads_q;
+  a.heads_kv = heads_kv;
+  a.seq_q = seq_q;
+  a.seq_k = seq_k;
+  a.head_dim = head_dim;
+  a.causal = causal ? 1 : 0;
+  a.c = (float)((double)scale * 1.4426950408889634);
+  a.workspace = workspace;
+  a.stream = (hipStream_t)stream;
+  a.plan = p;
+  hipError_t e;
+  switch (p.kernel) {
+    case OSX_KERNEL_PREFILL_BF16: e = osx::launch_prefill_bf16(a); break;
+    case OSX_KERNEL_PREFILL_F32: e = osx::launch_prefill_f32(a); break;
+    case OSX_KERNEL_DECODE_BF16: e = osx::launch_decode_bf16(a); break;
+    default: return fail(OSX_EUNSUPPORTED, "no kernel for plan %d", p.kernel);
+  }
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) return fail(OSX_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int osx_softmax_rows_plan(int64_t rows, int64_t cols, osx_plan* out) {
+  osx_plan p;
+  int st = plan_softmax(rows, cols, &p);
+  if (out) *out = p;
+  return st;
+}
+
+int osx_softmax_rows_workspace(int64_t rows, int64_t cols, size_t* bytes) {
+  osx_plan p;
+  int st = plan_softmax(rows, cols, &p);
+  if (bytes) *bytes = st == OSX_OK ? p.workspace_bytes : 0;
+  return st;
+}
+
+int osx_softmax_rows(const float* x, float* y, int64_t rows, int64_t cols, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  osx_plan p;
+  int st = plan_softmax(rows, cols, &p);
+  if (st != OSX_OK) return st;
+  if (p.kernel == OSX_KERNEL_NONE) return ok();
+  if (!x || !y) return fail(OSX_EINVAL, "null x or y pointer");
+  const size_t n = (size_t)rows * (size_t)cols * sizeof(float);
+  if (x != y && overlap(x, n, y, n)) return fail(OSX_EINVAL, "x and y overlap without being the same buffer");
+  if (p.workspace_bytes > 0 && (!workspace || workspace_bytes < p.workspace_bytes))
+    return fail(OSX_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : (size_t)0,
+                p.workspace_bytes);
+  if (p.workspace_bytes > 0 && (overlap(workspace, p.workspace_bytes, x, n) || overlap(workspace, p.workspace_bytes, y, n)))
+    return fail(OSX_EINVAL, "workspace overlaps x or y");
+  osx::SoftmaxArgs a;
+  a.x = x;
+  a.y = y;
+  a.rows = rows;
+  a.cols = cols;
+  a.workspace = workspace;
+  a.stream = (hipStream_t)stream;
+  a.plan = p;
+  hipError_t e = osx::launch_softmax_rows(a);
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) return fail(OSX_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+const char* osx_status_string(int status) {
+  switch (status) {
+    case OSX_OK: return "OSX_OK";
+    case OSX_EINVAL: return "OSX_EINVAL: invalid argument";
+    case OSX_EUNSUPPORTED: return "OSX_EUNSUPPORTED: valid but not implemented";
+    case OSX_EHIP: return "OSX_EHIP: HIP runtime error";
+    case OSX_EWORKSPACE: return "OSX_EWORKSPACE: workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+const char* osx_last_error(void) { return g_err; }
+
+int osx_version(void) { return 100; }
+
+}  // extern "C"

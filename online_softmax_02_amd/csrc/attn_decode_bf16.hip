@@ -1,0 +1,293 @@
+// Attention forward for one query token per sequence (decode), bf16, gfx950.
+//
+// The method is the same online recurrence (page "softmax_attention", section
+// 实现思路); the shape makes it a stream over K/V: every (batch, KV head) has
+// only G query vectors, so the work is bound by reading K and V once from HBM.
+//
+//  * One workgroup per (batch, KV head, split of the keys).  All G query heads
+//    of that KV head are packed into the 16 columns of a 16x16x32 MFMA tile, so
+//    every K/V byte is read once and serves all G heads.
+//  * Each of the 4 wavefronts walks its own 32-key blocks of the split with
+//    16-byte loads; two workgroups per CU keep enough loads in flight.  K feeds S^T = K Q^T directly from registers; V is written
+//    to the wavefront's LDS slice transposed (keys permuted so each lane's 8
+//    keys are one 16-byte read) and feeds O^T += V^T P^T.
+//  * The 4 wavefront states are merged in LDS and written as one partial
+//    (m, l, acc) per split.  A second kernel merges the splits of each query
+//    head with the rule of page "Softmax 算子的实现与优化", section Online
+//    Softmax, applied to partial states: m = max m_s, l = sum l_s 2^(m_s - m),
+//    acc = sum acc_s 2^(m_s - m), then O = acc / l.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace osx {
+namespace {
+
+constexpr int BN = kDecodeBlockN;  // 32 keys per wavefront step
+constexpr int NCOL = 16;           // MFMA columns available for query heads
+
+template <int D>
+struct DecTile {
+  static constexpr int CH = D / 8;        // 16-byte chunks per row
+  static constexpr int KC = D / 32;       // k-steps of the QK MFMA
+  static constexpr int DT = D / 16;       // 16-row d tiles of the PV MFMA
+  static constexpr int VT_BYTES = D * BN * 2;  // one wavefront's V^T slice
+  static constexpr int VU = 8 * CH / kWaveSize;  // (4 keys x 16 bytes) V units per lane
+};
+
+__device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// V^T row (64 bytes = 4 chunks of 8 keys) swizzle: 16 consecutive rows hit 16
+// distinct bank groups.
+__device__ __forceinline__ int vt_swz(int d) { return (d >> 2) & 3; }
+
+template <int D>
+struct Regs {
+  u32x4 k[2][DecTile<D>::KC];  // [sub-tile][k-step]
+  u32x4 v[DecTile<D>::VU][4];  // [unit][key in quad]
+};
+
+template <int D>
+__device__ __forceinline__ void load_regs(Regs<D>& R, const uint16_t* __restrict__ Kb,
+                                          const uint16_t* __restrict__ Vb, int j0, int k_end, int lane) {
+  using T = DecTile<D>;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  const int l16 = lane & 15, grp = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int j = j0 + 16 * t + l16;
+#pragma unroll
+    for (int kc = 0; kc < T::KC; ++kc) R.k[t][kc] = j < k_end ? ld16(Kb + (size_t)j * D + 32 * kc + 8 * grp) : z;
+  }
+#pragma unroll
+  for (int r = 0; r < T::VU; ++r) {
+    const int u = lane + kWaveSize * r;
+    const int kq = u / T::CH, ch = u % T::CH;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int j = j0 + 4 * kq + jj;
+      R.v[r][jj] = j < k_end ? ld16(Vb + (size_t)j * D + 8 * ch) : z;
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kAttnThreads, 2) void decode_bf16_kernel(
+    const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, const uint16_t* __restrict__ Vg,
+    float* __restrict__ ws, int Hq, int Hkv, int Sk, float c, int splits, int keys_per_split) {
+  using T = DecTile<D>;
+  // V^T slices during the stream; reused for the wavefront merge afterwards.
+  constexpr int MERGE_BYTES = kAttnWaves * NCOL * (D + 2) * 4;
+  constexpr int LDS_BYTES = kAttnWaves * T::VT_BYTES > MERGE_BYTES ? kAttnWaves * T::VT_BYTES : MERGE_BYTES;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, grp = lane >> 4;
+
+  const int split = blockIdx.x % splits;
+  const int bkv = blockIdx.x / splits;
+  const int b = bkv / Hkv, kvh = bkv % Hkv;
+  const int G = Hq / Hkv;
+
+  const int k_begin = split * keys_per_split;
+  int k_end = k_begin + keys_per_split;
+  if (k_end > Sk) k_end = Sk;
+
+  const uint16_t* Kb = Kg + (size_t)bkv * Sk * D;
+  const uint16_t* Vb = Vg + (size_t)bkv * Sk * D;
+
+  // Q^T as the B operand: column l16 is query head kvh*G + l16 (zero past G).
+  bf16x8 qop[T::KC];
+  {
+    const int hq = kvh * G + (l16 < G ? l16 : 0);
+    const uint16_t* qp = Qg + (size_t)(b * Hq + hq) * D;
+#pragma unroll
+    for (int kc = 0; kc < T::KC; ++kc) {
+      u32x4 x = ld16(qp + 32 * kc + 8 * grp);
+      if (l16 >= G) x = u32x4{0u, 0u, 0u, 0u};
+      qop[kc] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+
+  unsigned char* vt = lds + wave * T::VT_BYTES;
+  f32x4 acc[T::DT];
+#pragma unroll
+  for (int i = 0; i < T::DT; ++i) acc[i] = f32x4{};
+  float m_run = kNegInf, l_run = 0.f;
+
+  auto compute = [&](const Regs<D>& R, int j0) {
+    // ---- S^T = K Q^T: two 16-key sub-tiles; lane (col l16, grp) holds keys 16t + 4grp + j ----
+    f32x4 s[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int kc = 0; kc < T::KC; ++kc)
+        s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, R.k[t][kc]), qop[kc], s[t], 0, 0,
+                                                       0);
+    if (j0 + BN > k_end) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (j0 + 16 * t + 4 * grp + j >= k_end) s[t][j] = kNegInf;
+    }
+    float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx * c);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = exp2_fast(m_run - m_use);
+    // P is rounded to bf16 once; the PV MFMA and the denominator use the same values.
+    float p[8];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) p[4 * t + j] = exp2_fast(fmaf(s[t][j], c, -m_use));
+    const bf16x8 pb = pack_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+    l_run = sum_bf16x8(pb, l_run * alpha);
+    m_run = m_new;
+#pragma unroll
+    for (int i = 0; i < T::DT; ++i) acc[i] *= alpha;
+
+    // ---- stage V^T: VT[d][pos(key)], pos = 8*((key>>2)&3) + 4*(key>>4) + (key&3) ----
+#pragma unroll
+    for (int r = 0; r < T::VU; ++r) {
+      const int u = lane + kWaveSize * r;
+      const int kq = u / T::CH, ch = u % T::CH;
+      const int cc = kq & 3, half = kq >> 2;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int w = e >> 1;
+        uint32_t lo, hi;
+        if (e & 1) {
+          lo = (R.v[r][0][w] >> 16) | (R.v[r][1][w] & 0xffff0000u);
+          hi = (R.v[r][2][w] >> 16) | (R.v[r][3][w] & 0xffff0000u);
+        } else {
+          lo = (R.v[r][0][w] & 0xffffu) | (R.v[r][1][w] << 16);
+          hi = (R.v[r][2][w] & 0xffffu) | (R.v[r][3][w] << 16);
+        }
+        const int d = 8 * ch + e;
+        const u32x2 val = {lo, hi};
+        *reinterpret_cast<u32x2*>(vt + d * (BN * 2) + ((cc ^ vt_swz(d)) << 4) + 8 * half) = val;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // ---- O^T += V^T P^T: P^T lane (col, grp) element i is key 16(i/4) + 4grp + i%4 ----
+#pragma unroll
+    for (int dt = 0; dt < T::DT; ++dt) {
+      const int d = 16 * dt + l16;
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(vt + d * (BN * 2) + ((grp ^ vt_swz(d)) << 4));
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, acc[dt], 0, 0, 0);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  // ---- stream this wavefront's blocks: k_begin + BN*(wave + 4i) ----
+  for (int j0 = k_begin + BN * wave; j0 < k_end; j0 += BN * kAttnWaves) {
+    Regs<D> r;
+    load_regs<D>(r, Kb, Vb, j0, k_end, lane);
+    compute(r, j0);
+  }
+
+  // ---- merge the 4 wavefront states in LDS ----
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  __syncthreads();  // every wavefront is done with its V^T slice
+  float* ml = reinterpret_cast<float*>(lds);               // [wave][col][2]
+  float* accl = ml + kAttnWaves * NCOL * 2;                // [wave][col][D]
+  if (grp == 0) {
+    ml[(wave * NCOL + l16) * 2] = m_run;
+    ml[(wave * NCOL + l16) * 2 + 1] = l_run;
+  }
+#pragma unroll
+  for (int dt = 0; dt < T::DT; ++dt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) accl[(wave * NCOL + l16) * D + 16 * dt + 4 * grp + j] = acc[dt][j];
+  __syncthreads();
+
+  float* ws_ml = ws;
+  const size_t n_part = (size_t)gridDim.x * G;
+  float* ws_acc = ws + 2 * n_part;
+  const size_t part0 = (size_t)blockIdx.x * G;
+  for (int idx = tid; idx < G * D; idx += kAttnThreads) {
+    const int col = idx / D, dd = idx % D;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, ml[(w * NCOL + col) * 2]);
+    float lsum = 0.f, asum = 0.f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int w = 0; w < kAttnWaves; ++w) {
+        const float f = exp2_fast(ml[(w * NCOL + col) * 2] - M);
+        lsum += ml[(w * NCOL + col) * 2 + 1] * f;
+        asum += accl[(w * NCOL + col) * D + dd] * f;
+      }
+    }
+    ws_acc[(part0 + col) * D + dd] = asum;
+    if (dd == 0) {
+      ws_ml[(part0 + col) * 2] = M;
+      ws_ml[(part0 + col) * 2 + 1] = lsum;
+    }
+  }
+}
+
+// Merge the splits of one (batch, query head): O = sum acc_s 2^(m_s-m) / sum l_s 2^(m_s-m).
+template <int D>
+__global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restrict__ ws, uint16_t* __restrict__ Og,
+                                                           int Hq, int Hkv, int splits, int n_wg) {
+  const int bh = blockIdx.x;
+  const int b = bh / Hq, hq = bh % Hq;
+  const int G = Hq / Hkv;
+  const int kvh = hq / G, g = hq % G;
+  const int bkv = b * Hkv + kvh;
+  const size_t n_part = (size_t)n_wg * G;
+  const float* ws_ml = ws;
+  const float* ws_acc = ws + 2 * n_part;
+  const int dd = threadIdx.x;
+  float M = kNegInf;
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, ws_ml[((size_t)(bkv * splits + s) * G + g) * 2]);
+  float l = 0.f, a = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const size_t p = (size_t)(bkv * splits + s) * G + g;
+    const float f = exp2_fast(ws_ml[p * 2] - M);
+    l += ws_ml[p * 2 + 1] * f;
+    a += ws_acc[p * D + dd] * f;
+  }
+  const float o = a / l;
+  const uint32_t w = pack_bf16x2(o, 0.f);
+  Og[(size_t)bh * D + dd] = (uint16_t)(w & 0xffffu);
+}
+
+template <int D>
+hipError_t launch(const AttnArgs& a) {
+  const int splits = a.plan.splits;
+  int kps = (a.seq_k + splits - 1) / splits;
+  kps = (kps + BN - 1) / BN * BN;
+  float* ws = static_cast<float*>(a.workspace);
+  hipLaunchKernelGGL(decode_bf16_kernel<D>, dim3((unsigned)a.plan.grid), dim3(kAttnThreads), 0, a.stream,
+                     static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                     static_cast<const uint16_t*>(a.v), ws, a.heads_q, a.heads_kv, a.seq_k, a.c, splits, kps);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_combine_kernel<D>, dim3((unsigned)(a.batch * a.heads_q)), dim3(D), 0, a.stream, ws,
+                     static_cast<uint16_t*>(a.o), a.heads_q, a.heads_kv, splits, (int)a.plan.grid);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_bf16(const AttnArgs& a) {
+  switch (a.head_dim) {
+    case 64: return launch<64>(a);
+    case 128: return launch<128>(a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace osx

@@ -1,0 +1,242 @@
+// Single-pass attention forward, fp32 inputs and outputs, gfx950.
+//
+// Same method and mapping as the bf16 kernel (page "softmax_attention",
+// section 实现思路: blocks of keys, running max / denominator / accumulator,
+// rescale by 2^(m_old - m_new), ragged tail masked to -inf), in true fp32:
+// v_mfma_f32_32x32x2_f32 computes S^T = K Q^T and O^T += V^T P^T with IEEE
+// fp32 products and fp32 accumulation (no reduced-precision inputs; page
+// "从零开始写Qwen3（五-其一）使用Triton实现自注意力" notes that a TF32 shortcut
+// loses precision).
+//
+// Each MFMA lane supplies a single k value, so P^T comes straight from the
+// score registers and V is read from a plain row-major LDS block.  The head
+// dimension d (a multiple of 4, at most 128) is padded with zeros up to DP,
+// a multiple of 32; padded columns are never stored.  Blocks are 32 keys.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace osx {
+namespace {
+
+constexpr int BN = kF32BlockN;  // 32 keys per block
+
+template <int DP>
+struct F32Tile {
+  static constexpr int CH = DP / 4;                 // 16-byte chunks per K row
+  static constexpr int HALF = DP / 2;               // d values per MFMA half-wave
+  static constexpr int DT = DP / 32;                // 32-row d tiles of the PV MFMA
+  static constexpr int VSTRIDE = DP + 8;            // padded V row (floats)
+  static constexpr int K_BYTES = BN * DP * 4;
+  static constexpr int V_BYTES = BN * VSTRIDE * 4;
+  static constexpr int BUF = K_BYTES + V_BYTES;
+  static constexpr int UNITS = BN * CH;             // 16-byte units per block (K or V)
+  static constexpr int PER_T = (UNITS + kAttnThreads - 1) / kAttnThreads;
+};
+
+template <int CH>
+__device__ __forceinline__ int k_swz(int row) {
+  return CH % 16 == 0 ? (row & 15) : ((row >> 1) & 7);
+}
+
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+
+template <int DP>
+__global__ __launch_bounds__(kAttnThreads, 2) void prefill_f32_kernel(
+    const float* __restrict__ Qg, const float* __restrict__ Kg, const float* __restrict__ Vg, float* __restrict__ Og,
+    int Hq, int Hkv, int Sq, int Sk, int d, int causal, float c, int hp, int n_hgroups, int n_qtiles,
+    int units_per_tile) {
+  using T = F32Tile<DP>;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * T::BUF];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+
+  int qt = blockIdx.x / units_per_tile;
+  const int rem = blockIdx.x - qt * units_per_tile;
+  if (causal) qt = n_qtiles - 1 - qt;
+  const int G = Hq / Hkv;
+  const int b = rem / (Hkv * n_hgroups);
+  const int kvh = (rem / n_hgroups) % Hkv;
+  const int hg = rem % n_hgroups;
+  const int rs = kAttnWaves / hp;
+  const int head = kvh * G + hg * hp + (wave % hp);
+  const int wg_row0 = qt * kRowsPerWave * rs;
+  const int row0 = wg_row0 + (wave / hp) * kRowsPerWave;
+  const int q = row0 + l32;
+  const int qc = q < Sq ? q : Sq - 1;
+
+  const size_t q_base = (size_t)(b * Hq + head) * Sq * d;
+  const size_t kv_base = (size_t)(b * Hkv + kvh) * Sk * d;
+  const float* Kb = Kg + kv_base;
+  const float* Vb = Vg + kv_base;
+
+  // Q as the B operand: lane (query l32, half hf) holds d = hf*DP/2 + j.
+  float qv[T::HALF];
+#pragma unroll
+  for (int j = 0; j < T::HALF; j += 4) {
+    const int col = hf * T::HALF + j;
+    const f32x4 x = col < d ? ld4(Qg + q_base + (size_t)qc * d + col) : f32x4{};
+    qv[j] = x.x;
+    qv[j + 1] = x.y;
+    qv[j + 2] = x.z;
+    qv[j + 3] = x.w;
+  }
+
+  int wg_row_end = wg_row0 + kRowsPerWave * rs;
+  if (wg_row_end > Sq) wg_row_end = Sq;
+  const bool cmask = causal && Sq > 1;
+  const int n_keys = cmask ? (wg_row_end < Sk ? wg_row_end : Sk) : Sk;
+  const int nblk = (n_keys + BN - 1) / BN;
+  const int wave_row_last = row0 + kRowsPerWave - 1;
+
+  f32x4 kst[T::PER_T], vst[T::PER_T];
+  auto load_block = [&](int j0) {
+#pragma unroll
+    for (int r = 0; r < T::PER_T; ++r) {
+      const int u = tid + kAttnThreads * r;
+      const int key = u / T::CH, col = (u % T::CH) * 4;
+      const int j = j0 + key;
+      const bool ok = u < T::UNITS && j < Sk && col < d;
+      kst[r] = ok ? ld4(Kb + (size_t)j * d + col) : f32x4{};
+      vst[r] = ok ? ld4(Vb + (size_t)j * d + col) : f32x4{};
+    }
+  };
+  auto store_block = [&](int buf) {
+    unsigned char* kl = lds + buf * T::BUF;
+    float* vl = reinterpret_cast<float*>(kl + T::K_BYTES);
+#pragma unroll
+    for (int r = 0; r < T::PER_T; ++r) {
+      const int u = tid + kAttnThreads * r;
+      if (u < T::UNITS) {
+        const int key = u / T::CH, ch = u % T::CH;
+        *reinterpret_cast<f32x4*>(kl + key * (DP * 4) + ((ch ^ k_swz<T::CH>(key)) << 4)) = kst[r];
+        *reinterpret_cast<f32x4*>(vl + key * T::VSTRIDE + ch * 4) = vst[r];
+      }
+    }
+  };
+
+  f32x16 acc[T::DT];
+#pragma unroll
+  for (int i = 0; i < T::DT; ++i) acc[i] = f32x16{};
+  float m_run = kNegInf, l_run = 0.f;
+
+  if (nblk > 0) {
+    load_block(0);
+    store_block(0);
+  }
+  __syncthreads();
+
+  for (int jb = 0; jb < nblk; ++jb) {
+    const int j0 = jb * BN;
+    const bool has_next = jb + 1 < nblk;
+    if (has_next) load_block(j0 + BN);
+
+    const bool active = !(cmask && j0 > wave_row_last);
+    if (active) {
+      const unsigned char* kl = lds + (jb & 1) * T::BUF;
+      const float* vl = reinterpret_cast<const float*>(kl + T::K_BYTES);
+
+      // S^T = K Q^T over the padded head dimension
+      f32x16 s = f32x16{};
+#pragma unroll
+      for (int j = 0; j < T::HALF; j += 4) {
+        const int ch = (hf * T::HALF + j) >> 2;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(kl + l32 * (DP * 4) + ((ch ^ k_swz<T::CH>(l32)) << 4));
+        s = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, qv[j], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, qv[j + 1], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, qv[j + 2], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, qv[j + 3], s, 0, 0, 0);
+      }
+
+      const bool need_mask = (j0 + BN > Sk) || (cmask && j0 + BN - 1 > row0);
+      if (need_mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kidx = j0 + 8 * (r >> 2) + 4 * hf + (r & 3);
+          const bool ok = kidx < Sk && (!cmask || kidx <= q);
+          s[r] = ok ? s[r] : kNegInf;
+        }
+      }
+
+      float mx = s[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run, mx * c);
+      const float m_use = m_new == kNegInf ? 0.f : m_new;
+      const float alpha = exp2_fast(m_run - m_use);
+      float rsum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2_fast(fmaf(s[r], c, -m_use));
+        s[r] = p;
+        rsum += p;
+      }
+      l_run = l_run * alpha + rsum;
+      m_run = m_new;
+      if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+        for (int i = 0; i < T::DT; ++i) acc[i] *= alpha;
+      }
+
+      // O^T += V^T P^T: lane (d, hf) reads V[key(r, hf)][d]
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 8 * (r >> 2) + 4 * hf + (r & 3);
+#pragma unroll
+        for (int dt = 0; dt < T::DT; ++dt) {
+          const float a = vl[key * T::VSTRIDE + 32 * dt + l32];
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[r], acc[dt], 0, 0, 0);
+        }
+      }
+    }
+
+    if (has_next) store_block((jb + 1) & 1);
+    __syncthreads();
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = 1.0f / l_tot;
+  if (q < Sq) {
+    float* op = Og + q_base + (size_t)q * d;
+#pragma unroll
+    for (int dt = 0; dt < T::DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * dt + 8 * g + 4 * hf;
+        if (d0 < d) {
+          const f32x4 w = {acc[dt][4 * g] * inv, acc[dt][4 * g + 1] * inv, acc[dt][4 * g + 2] * inv,
+                           acc[dt][4 * g + 3] * inv};
+          *reinterpret_cast<f32x4*>(op + d0) = w;
+        }
+      }
+  }
+}
+
+template <int DP>
+hipError_t launch(const AttnArgs& a) {
+  const int G = a.heads_q / a.heads_kv;
+  const int hp = a.plan.heads_per_wg;
+  const int n_hgroups = G / hp;
+  const int rows_per_wg = a.plan.block_m;
+  const int n_qtiles = (a.seq_q + rows_per_wg - 1) / rows_per_wg;
+  const int units_per_tile = a.batch * a.heads_kv * n_hgroups;
+  hipLaunchKernelGGL(prefill_f32_kernel<DP>, dim3((unsigned)a.plan.grid), dim3(kAttnThreads), 0, a.stream,
+                     static_cast<const float*>(a.q), static_cast<const float*>(a.k), static_cast<const float*>(a.v),
+                     static_cast<float*>(a.o), a.heads_q, a.heads_kv, a.seq_q, a.seq_k, a.head_dim, a.causal, a.c, hp,
+                     n_hgroups, n_qtiles, units_per_tile);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_f32(const AttnArgs& a) {
+  if (a.head_dim <= 32) return launch<32>(a);
+  if (a.head_dim <= 64) return launch<64>(a);
+  if (a.head_dim <= 96) return launch<96>(a);
+  if (a.head_dim <= 128) return launch<128>(a);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace osx

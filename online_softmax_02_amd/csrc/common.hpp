@@ -1,0 +1,74 @@
+// Device helpers shared by the gfx950 kernels: vector types, exp2, wave64
+// reductions and bf16 packing.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace osx {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;  // MFMA bf16 operand: 8 values per lane
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// 2^x on the transcendental unit (v_exp_f32); exp2(-inf) = 0.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Butterfly reductions over all 64 lanes of a wavefront.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Merge two online-softmax states (m, l) whose m is in the log2 domain:
+// l = l_a 2^(m_a - m) + l_b 2^(m_b - m), m = max(m_a, m_b).  Empty states
+// carry m = -inf, l = 0.
+__device__ __forceinline__ void merge_ml(float& m, float& l, float mb, float lb) {
+  float mn = fmaxf(m, mb);
+  if (mn == kNegInf) return;  // both empty
+  l = l * exp2_fast(m - mn) + lb * exp2_fast(mb - mn);
+  m = mn;
+}
+
+// Two fp32 -> packed bf16 (round to nearest even) in one 32-bit word.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  f32x2 v = {a, b};
+  bf16x2 h = __builtin_convertvector(v, bf16x2);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, float a3, float a4, float a5, float a6,
+                                              float a7) {
+  u32x4 u = {pack_bf16x2(a0, a1), pack_bf16x2(a2, a3), pack_bf16x2(a4, a5), pack_bf16x2(a6, a7)};
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// Sum of the 8 bf16 values of an MFMA operand added to `acc`, on the dot2
+// unit: each v_dot2_f32_bf16 adds a pair times (1, 1).
+__device__ __forceinline__ float sum_bf16x8(bf16x8 v, float acc) {
+  const u32x4 u = __builtin_bit_cast(u32x4, v);
+  const bf16x2 one = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u[0]), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u[1]), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u[2]), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u[3]), one, acc, false);
+  return acc;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+}  // namespace osx

@@ -1,0 +1,52 @@
+// Host-side interface between the C ABI (abi.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "osx.h"
+
+namespace osx {
+
+// Tile constants shared by the planner and the kernels.
+constexpr int kWaveSize = 64;
+constexpr int kAttnThreads = 256;     // 4 wavefronts per workgroup
+constexpr int kAttnWaves = 4;
+constexpr int kRowsPerWave = 32;      // query rows per wavefront (one 32-wide MFMA column tile)
+constexpr int kBf16BlockN = 64;       // keys per LDS block, bf16 prefill
+constexpr int kF32BlockN = 32;        // keys per LDS block, fp32 prefill
+constexpr int kDecodeBlockN = 32;     // keys per wavefront step, decode
+constexpr int kDecodeMaxGroup = 16;   // query heads per KV head the decode kernel can pack
+constexpr int kDecodeTargetWgs = 4096;
+constexpr int kSoftmaxThreads = 256;
+constexpr int64_t kSoftmaxRowMax = 8192;   // longest row handled by one workgroup
+constexpr int64_t kSoftmaxChunk = 16384;   // elements per workgroup when a row is split
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  int batch, heads_q, heads_kv, seq_q, seq_k, head_dim, causal;
+  float c;  // scale * log2(e): scores are exponentiated as 2^(s*c - m)
+  void* workspace;
+  hipStream_t stream;
+  osx_plan plan;
+};
+
+struct SoftmaxArgs {
+  const float* x;
+  float* y;
+  int64_t rows, cols;
+  void* workspace;
+  hipStream_t stream;
+  osx_plan plan;
+};
+
+hipError_t launch_prefill_bf16(const AttnArgs& a);
+hipError_t launch_prefill_f32(const AttnArgs& a);
+hipError_t launch_decode_bf16(const AttnArgs& a);
+hipError_t launch_softmax_rows(const SoftmaxArgs& a);
+
+}  // namespace osx

@@ -1,0 +1,37 @@
+"""Helpers for the GPU tests: host<->device transfer and the parity bars."""
+import numpy as np
+
+import oracle
+
+# Parity bars: fp32 max abs error 1e-5; bf16 |err| <= 2e-2 + 1e-2 |ref| per element.
+F32_ATOL = 1e-5
+BF16_ATOL, BF16_RTOL = 2e-2, 1e-2
+
+
+def to_dev(a: np.ndarray, device="cuda"):
+    import torch
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+
+def to_f64(t) -> np.ndarray:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return oracle.bf16_bits_to_f64(t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16))
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+def check(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = "") -> float:
+    """Assert the parity bar; returns the max abs error."""
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite outputs"
+    err = np.abs(got - ref)
+    if dtype == "f32":
+        worst = float(err.max()) if err.size else 0.0
+        assert worst <= F32_ATOL, f"{what}: max abs error {worst:.3e} > {F32_ATOL}"
+    else:
+        bound = BF16_ATOL + BF16_RTOL * np.abs(ref)
+        bad = err > bound
+        assert not bad.any(), f"{what}: {int(bad.sum())} elements outside 2e-2 + 1e-2|ref|, worst {err.max():.3e}"
+    return float(err.max()) if err.size else 0.0

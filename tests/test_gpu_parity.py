@@ -1,0 +1,250 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small and mid sizes are compared element by element; the full-size workloads
+either in full (when the oracle takes seconds) or on sampled rows that the
+oracle computes one by one.  Bars: fp32 max abs 1e-5; bf16 2e-2 + 1e-2|ref|.
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import check, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def osx():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import online_softmax_02_amd
+    return online_softmax_02_amd
+
+
+def _run_attn(osx, t, dtype, causal, poison=True):
+    q, k, v = to_dev(t["q"]), to_dev(t["k"]), to_dev(t["v"])
+    out = torch.empty_like(q)
+    if poison:
+        out.fill_(float("nan"))
+    osx.attn_fwd(q, k, v, causal=causal, out=out)
+    torch.cuda.synchronize()
+    return to_f64(out)
+
+
+# ------------------------------------------------------------------ workloads in full
+def test_attn_f32_m64_n100_d48(osx):
+    w = synth.WORKLOADS["attn_f32_m64_n100_d48"]
+    t = synth.attn_inputs(w)
+    print(f"case {w.name}", flush=True)
+    got = _run_attn(osx, t, "f32", False)
+    check(got, oracle.attention(t["q"], t["k"], t["v"]), "f32", w.name)
+
+
+def test_attn_f32_4k_d128_planted_key(osx):
+    w = synth.WORKLOADS["attn_f32_4k_d128"]
+    t = synth.attn_inputs(w)
+    print(f"case {w.name}", flush=True)
+    got = _run_attn(osx, t, "f32", False)
+    ref = oracle.attention(t["q"], t["k"], t["v"])
+    err = check(got, ref, "f32", w.name)
+    print(f"{w.name}: max abs err {err:.3e}")
+    # rows where the planted key carries > 0.99 of the weight return ~V[3900]
+    q, k = t["q"][0, 0].astype(np.float64), t["k"][0, 0].astype(np.float64)
+    s = q @ k.T / np.sqrt(w.head_dim)
+    wts = np.exp(s - s.max(axis=1, keepdims=True))
+    wts /= wts.sum(axis=1, keepdims=True)
+    rows = np.nonzero(wts[:, 3900] > 0.99)[0]
+    assert rows.size > 10
+    vmax = np.abs(t["v"][0, 0]).max()
+    dev = np.abs(got[0, 0, rows] - t["v"][0, 0, 3900][None, :]).max(axis=1)
+    assert (dev <= (1 - wts[rows, 3900]) * 2 * vmax + 1e-5).all()
+
+
+def test_softmax_4x200(osx):
+    w = synth.WORKLOADS["softmax_4x200"]
+    x = synth.softmax_inputs(w)
+    print(f"case {w.name}", flush=True)
+    y = osx.softmax_rows(to_dev(x))
+    torch.cuda.synchronize()
+    check(to_f64(y), oracle.softmax_rows(x), "f32", w.name)
+
+
+def test_softmax_1x16m_late_spike(osx):
+    w = synth.WORKLOADS["softmax_1x16m"]
+    x = synth.softmax_inputs(w)
+    print(f"case {w.name}", flush=True)
+    xd = to_dev(x)
+    y = torch.full_like(xd, float("nan"))
+    osx.softmax_rows(xd, out=y)
+    torch.cuda.synchronize()
+    got = to_f64(y)
+    ref = oracle.softmax_rows(x)
+    check(got, ref, "f32", w.name)
+    idx = int(np.argmax(x[0]))
+    assert got[0, idx] == pytest.approx(ref[0, idx], abs=1e-6)
+    # diagnostic: relative error over all (normal, tiny) outputs
+    rel = np.abs(got - ref) / ref
+    print(f"{w.name}: max rel err {rel.max():.3e}")
+    assert rel.max() < 1e-4
+
+
+def test_gqa_prefill_bf16_full_size_sampled_rows(osx):
+    w = synth.WORKLOADS["gqa_prefill_bf16"]
+    t = synth.attn_inputs(w)
+    print(f"case {w.name}", flush=True)
+    got = _run_attn(osx, t, "bf16", True)
+    G = w.groups
+    rng = np.random.default_rng(7)
+    rows = sorted(set([0, 1, 31, 32, 33, 63, 64, 65, 127, 128, 2047, 2048, 4062, 4063, 4064, 4095]
+                      + rng.integers(0, w.seq_q, 16).tolist()))
+    heads = [(0, 0), (0, 3), (0, 4), (0, 31), (1, 0), (1, 17), (1, 30)]
+    for b, h in heads:
+        ref = oracle.attention_rows(t["q"][b, h, rows], t["k"][b, h // G], t["v"][b, h // G], rows, causal=True,
+                                    seq_q=w.seq_q)
+        check(got[b, h, rows], ref, "bf16", f"{w.name} b={b} h={h}")
+
+
+def test_gqa_decode_bf16_full_size_sampled_heads(osx):
+    w = synth.WORKLOADS["gqa_decode_bf16"]
+    t = synth.attn_inputs(w)
+    print(f"case {w.name}", flush=True)
+    got = _run_attn(osx, t, "bf16", False)
+    G = w.groups
+    errs = []
+    for b in (0, 1, 37, 63):
+        for h in (0, 1, 5, 30, 31):
+            ref = oracle.attention_rows(t["q"][b, h], t["k"][b, h // G], t["v"][b, h // G], [0])
+            errs.append(check(got[b, h], ref, "bf16", f"{w.name} b={b} h={h}"))
+            rms = np.sqrt(np.mean(ref ** 2))
+            assert np.abs(got[b, h] - ref).max() / rms < 2e-2
+    print(f"{w.name}: max abs err {max(errs):.3e}")
+
+
+# ------------------------------------------------------------------ mid sizes, element by element
+PREFILL_CASES = [
+    # dtype, B, Hq, Hkv, Sq, Sk, D, causal
+    ("bf16", 1, 4, 1, 200, 200, 128, True),     # G=4: 4 heads per workgroup, ragged tiles
+    ("bf16", 1, 4, 2, 150, 333, 128, False),    # G=2, Sq != Sk, ragged key tail
+    ("bf16", 2, 3, 3, 130, 130, 64, True),      # MHA, D=64, 128-row tiles
+    ("bf16", 1, 8, 1, 97, 97, 128, True),       # G=8: two head groups
+    ("bf16", 1, 2, 1, 1, 77, 128, False),       # Sq=1 through the decode path
+    ("bf16", 1, 40, 2, 1, 300, 128, True),      # G=20 > 16: Sq=1 falls back to the prefill kernel
+    ("f32", 1, 1, 1, 65, 257, 48, False),
+    ("f32", 1, 2, 1, 100, 100, 128, True),
+    ("f32", 2, 4, 2, 33, 90, 4, False),
+    ("f32", 1, 3, 3, 64, 64, 96, True),
+    ("f32", 1, 1, 1, 1, 5, 32, True),
+    ("f32", 1, 2, 2, 40, 1, 64, False),         # a single key
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_attention_mid_sizes(osx, case):
+    dtype, B, Hq, Hkv, Sq, Sk, D, causal = case
+    print(f"case {case}", flush=True)
+    t = synth.random_attn(zlib.crc32(str(case).encode()) % 1000, dtype, B, Hq, Hkv, Sq, Sk, D)
+    got = _run_attn(osx, t, dtype, causal)
+    check(got, oracle.attention(t["q"], t["k"], t["v"], causal=causal), dtype, str(case))
+
+
+DECODE_CASES = [
+    # B, Hq, Hkv, Sk, D
+    (2, 8, 2, 1, 128), (1, 4, 4, 31, 128), (3, 16, 1, 33, 128), (2, 10, 2, 1000, 64), (1, 8, 8, 5000, 128),
+    (4, 32, 8, 2049, 128), (1, 2, 1, 129, 64),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_decode_mid_sizes(osx, case):
+    B, Hq, Hkv, Sk, D = case
+    print(f"case decode {case}", flush=True)
+    assert osx.attn_plan(osx.OSX_BF16, B, Hq, Hkv, 1, Sk, D)["kernel_name"] == "decode_bf16"
+    t = synth.random_attn(sum(case), "bf16", B, Hq, Hkv, 1, Sk, D)
+    got = _run_attn(osx, t, "bf16", False)
+    check(got, oracle.attention(t["q"], t["k"], t["v"]), "bf16", f"decode {case}")
+
+
+SOFTMAX_CASES = [(1, 1), (3, 7), (5, 4), (2, 255), (1, 8192), (2, 8193), (3, 16384 * 2 + 5), (2, 100000),
+                 (64, 1000), (1, 1 << 20)]
+
+
+@pytest.mark.parametrize("shape", SOFTMAX_CASES, ids=lambda s: f"{s[0]}x{s[1]}")
+def test_softmax_shapes(osx, shape):
+    print(f"case softmax {shape}", flush=True)
+    x = np.random.default_rng(shape[1]).normal(0, 3, shape).astype(np.float32)
+    y = osx.softmax_rows(to_dev(x))
+    torch.cuda.synchronize()
+    check(to_f64(y), oracle.softmax_rows(x), "f32", f"softmax {shape}")
+
+
+def test_softmax_in_place_and_shift(osx):
+    x = np.random.default_rng(3).normal(0, 2, (4, 40000)).astype(np.float32)
+    xd = to_dev(x)
+    osx.softmax_rows(xd, out=xd)
+    x_shift = x + np.float32(500.0)
+    ys = osx.softmax_rows(to_dev(x_shift))
+    torch.cuda.synchronize()
+    check(to_f64(xd), oracle.softmax_rows(x), "f32", "in place")
+    check(to_f64(ys), oracle.softmax_rows(x_shift), "f32", "shifted by 500")
+
+
+# ------------------------------------------------------------------ exact index maps
+@pytest.mark.parametrize("dtype,S,D", [("bf16", 300, 128), ("f32", 300, 64), ("bf16", 129, 64)])
+def test_causal_index_map_exact(osx, dtype, S, D):
+    """K = 0: visible weights are uniform; V[j, c] = bit c of j gives O[i, c] = #{j <= i: bit c} / (i+1)."""
+    j = np.arange(S)
+    bits = ((j[:, None] >> (np.arange(D)[None, :] % 9)) & 1).astype(np.float32)
+    q = np.random.default_rng(1).normal(size=(1, 2, S, D)).astype(np.float32)
+    k = np.zeros((1, 1, S, D), np.float32)
+    v = np.broadcast_to(bits, (1, 1, S, D)).copy()
+    if dtype == "bf16":
+        q, k, v = (synth.round_to_bf16_bits(a) for a in (q, k, v))
+    got = _run_attn(osx, {"q": q, "k": k, "v": v}, dtype, True)
+    expect = np.cumsum(bits.astype(np.float64), axis=0) / (j[:, None] + 1)
+    tol = 2.0 ** -8 * np.abs(expect) + 1e-7 if dtype == "bf16" else 1e-6
+    for h in range(2):
+        assert (np.abs(got[0, h] - expect) <= tol).all(), f"causal map wrong for head {h}"
+
+
+@pytest.mark.parametrize("dtype,Sq", [("bf16", 70), ("bf16", 1), ("f32", 40)])
+def test_gqa_index_map_exact(osx, dtype, Sq):
+    """V[b, kv] = 8b + kv gives O[b, h] = 8b + h // G exactly."""
+    B, Hq, Hkv, Sk, D = 2, 16, 4, 90, 64
+    rng = np.random.default_rng(2)
+    q = rng.normal(size=(B, Hq, Sq, D)).astype(np.float32)
+    k = rng.normal(size=(B, Hkv, Sk, D)).astype(np.float32)
+    v = np.empty((B, Hkv, Sk, D), np.float32)
+    for b in range(B):
+        for kv in range(Hkv):
+            v[b, kv] = 8 * b + kv
+    if dtype == "bf16":
+        q, k, v = (synth.round_to_bf16_bits(a) for a in (q, k, v))
+    got = _run_attn(osx, {"q": q, "k": k, "v": v}, dtype, False)
+    for b in range(B):
+        for h in range(Hq):
+            np.testing.assert_array_equal(got[b, h], 8 * b + h // (Hq // Hkv))
+
+
+# ------------------------------------------------------------------ properties
+def test_deterministic_and_stream(osx):
+    t = synth.random_attn(5, "bf16", 1, 8, 2, 256, 256, 128)
+    q, k, v = to_dev(t["q"]), to_dev(t["k"]), to_dev(t["v"])
+    a = osx.attn_fwd(q, k, v, causal=True)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        b = osx.attn_fwd(q, k, v, causal=True)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_empty_problems_launch_nothing(osx):
+    q = torch.empty((0, 4, 16, 128), dtype=torch.bfloat16, device="cuda")
+    k = torch.empty((0, 1, 16, 128), dtype=torch.bfloat16, device="cuda")
+    assert osx.attn_fwd(q, k, k).shape == q.shape
+    x = torch.empty((0, 5), dtype=torch.float32, device="cuda")
+    assert osx.softmax_rows(x).shape == (0, 5)
