@@ -39,6 +39,14 @@ class OsxError(RuntimeError):
 
 
 def _load() -> ctypes.CDLL:
+    # libosx.so links libamdhip64.so.7.  PyTorch ships its own copy of that
+    # runtime; loading torch first makes the library bind to the same runtime
+    # instead of pulling a second one into the process (two HIP runtimes in one
+    # process do not share devices, streams or allocations).
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python -m online_softmax_02_amd.build` "
                           "(hipcc for gfx950); there is no fallback implementation")

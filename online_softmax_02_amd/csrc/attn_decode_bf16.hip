@@ -144,8 +144,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void decode_bf16_kernel(
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int j = 0; j < 4; ++j) p[4 * t + j] = exp2_fast(fmaf(s[t][j], c, -m_use));
-    const bf16x8 pb = pack_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-    l_run = sum_bf16x8(pb, l_run * alpha);
+    l_run *= alpha;
+    const bf16x8 pb = pack_bf16x8_sum(p, l_run);
     m_run = m_new;
 #pragma unroll
     for (int i = 0; i < T::DT; ++i) acc[i] *= alpha;

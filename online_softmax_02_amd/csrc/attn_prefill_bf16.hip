@@ -232,8 +232,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_bf16_kernel(
           float p[8];
 #pragma unroll
           for (int i = 0; i < 8; ++i) p[i] = exp2_fast(fmaf(s[t][8 * u + i], c, -m_use));
-          pb[t][u] = pack_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-          rsum = sum_bf16x8(pb[t][u], rsum);
+          pb[t][u] = pack_bf16x8_sum(p, rsum);
         }
       l_run = l_run * alpha + rsum;
       m_run = m_new;

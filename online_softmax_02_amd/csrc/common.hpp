@@ -56,16 +56,21 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, floa
   return __builtin_bit_cast(bf16x8, u);
 }
 
-// Sum of the 8 bf16 values of an MFMA operand added to `acc`, on the dot2
-// unit: each v_dot2_f32_bf16 adds a pair times (1, 1).
-__device__ __forceinline__ float sum_bf16x8(bf16x8 v, float acc) {
-  const u32x4 u = __builtin_bit_cast(u32x4, v);
+// Eight fp32 values rounded to bf16 (nearest even) and packed as an MFMA
+// operand, with their sum (of the rounded values) added to `acc` on the dot2
+// unit: each v_dot2_f32_bf16 adds one packed pair times (1, 1).  The pairs are
+// summed from the packed 32-bit words themselves, not extracted back out of
+// the bf16x8 vector.
+__device__ __forceinline__ bf16x8 pack_bf16x8_sum(const float (&p)[8], float& acc) {
   const bf16x2 one = __builtin_bit_cast(bf16x2, 0x3f803f80u);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u[0]), one, acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u[1]), one, acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u[2]), one, acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u[3]), one, acc, false);
-  return acc;
+  const uint32_t w0 = pack_bf16x2(p[0], p[1]), w1 = pack_bf16x2(p[2], p[3]);
+  const uint32_t w2 = pack_bf16x2(p[4], p[5]), w3 = pack_bf16x2(p[6], p[7]);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), one, acc, false);
+  const u32x4 u = {w0, w1, w2, w3};
+  return __builtin_bit_cast(bf16x8, u);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
