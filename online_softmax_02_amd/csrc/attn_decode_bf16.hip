@@ -46,27 +46,25 @@ struct Regs {
   u32x4 v[DecTile<D>::VU][4];  // [unit][key in quad]
 };
 
+// Keys past Sk read as zeros (buffer range); keys past the split's end are
+// real data that the score mask removes (their weights are exactly 0).
 template <int D>
-__device__ __forceinline__ void load_regs(Regs<D>& R, const uint16_t* __restrict__ Kb,
-                                          const uint16_t* __restrict__ Vb, int j0, int k_end, int lane) {
+__device__ __forceinline__ void load_regs(Regs<D>& R, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr, int j0,
+                                          int lane) {
   using T = DecTile<D>;
-  const u32x4 z = {0u, 0u, 0u, 0u};
   const int l16 = lane & 15, grp = lane >> 4;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int j = j0 + 16 * t + l16;
 #pragma unroll
-    for (int kc = 0; kc < T::KC; ++kc) R.k[t][kc] = j < k_end ? ld16(Kb + (size_t)j * D + 32 * kc + 8 * grp) : z;
+    for (int kc = 0; kc < T::KC; ++kc) R.k[t][kc] = buf_ld16(kr, (uint32_t)(j * D + 32 * kc + 8 * grp) * 2);
   }
 #pragma unroll
   for (int r = 0; r < T::VU; ++r) {
     const int u = lane + kWaveSize * r;
     const int kq = u / T::CH, ch = u % T::CH;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int j = j0 + 4 * kq + jj;
-      R.v[r][jj] = j < k_end ? ld16(Vb + (size_t)j * D + 8 * ch) : z;
-    }
+    for (int jj = 0; jj < 4; ++jj) R.v[r][jj] = buf_ld16(vr, (uint32_t)((j0 + 4 * kq + jj) * D + 8 * ch) * 2);
   }
 }
 
@@ -81,7 +79,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void decode_bf16_kernel(
   __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, grp = lane >> 4;
 
   const int split = blockIdx.x % splits;
@@ -93,8 +92,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void decode_bf16_kernel(
   int k_end = k_begin + keys_per_split;
   if (k_end > Sk) k_end = Sk;
 
-  const uint16_t* Kb = Kg + (size_t)bkv * Sk * D;
-  const uint16_t* Vb = Vg + (size_t)bkv * Sk * D;
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(Kg + (size_t)bkv * Sk * D, (uint32_t)Sk * D * 2);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(Vg + (size_t)bkv * Sk * D, (uint32_t)Sk * D * 2);
 
   // Q^T as the B operand: column l16 is query head kvh*G + l16 (zero past G).
   bf16x8 qop[T::KC];
@@ -191,7 +190,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void decode_bf16_kernel(
   // ---- stream this wavefront's blocks: k_begin + BN*(wave + 4i) ----
   for (int j0 = k_begin + BN * wave; j0 < k_end; j0 += BN * kAttnWaves) {
     Regs<D> r;
-    load_regs<D>(r, Kb, Vb, j0, k_end, lane);
+    load_regs<D>(r, kr, vr, j0, lane);
     compute(r, j0);
   }
 

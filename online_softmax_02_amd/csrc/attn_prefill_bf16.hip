@@ -13,20 +13,24 @@
 //    query head; the workgroup's wavefronts share one KV head (GQA: query head h
 //    reads KV head h / G), either 4 heads x 32 rows, 2 x 64 or 1 x 128.
 //  * K and V blocks of 64 keys are staged through LDS (double buffered, one
-//    barrier per block) with 16-byte global loads.
+//    barrier per block) with 16-byte buffer loads; rows past the end read as 0.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
-//    a lane then holds 16 keys of ONE query, so the row max and row sum are
-//    mostly lane-local (one cross-half exchange for the max per block) and the
+//    a lane then holds 16 scores of ONE query, so the row max and row sum are
+//    lane-local (plus one cross-half exchange for the max per block) and the
 //    rescale factor is a per-lane scalar.
-//  * The output is also accumulated transposed, O^T += V^T P^T, with the
-//    probabilities P (rounded to bf16) taken straight from the score registers
-//    as the B operand.  V is written to LDS transposed, with its keys permuted
-//    so each lane's 8 keys are one 16-byte read.
+//  * The output is also accumulated transposed, O^T += V^T P^T, with P (rounded
+//    to bf16 once) taken straight from the score registers as the B operand.
+//    V stays row-major in LDS; ds_read_b64_tr_b16 delivers it transposed.
 //  * exp is 2^(s*c - m) with c = scale*log2(e) folded into one FMA; m lives in
-//    that log2 domain.
+//    that log2 domain.  The reference m used in the exponent is moved (and acc,
+//    l rescaled by 2^(m_old - m_new)) only when a row's running max exceeds it
+//    by more than 2^8; the result is identical in exact arithmetic (the page's
+//    shift invariance) and the exponentials stay <= 2^8.
 //  * Causal: key blocks wholly after the workgroup's last query are never
-//    visited, only blocks that straddle the diagonal are masked, and tiles are
-//    dispatched heaviest first.
+//    visited; blocks that need no mask (the prefix before the diagonal) run a
+//    mask-free copy of the loop body; tiles are dispatched heaviest first.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -34,34 +38,36 @@ namespace osx {
 namespace {
 
 constexpr int BN = kBf16BlockN;  // 64 keys per block
+constexpr float kRescaleSlack = 8.0f;  // log2 units a row max may exceed the reference before a rescale
+
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(8))) short i16x8;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 template <int D>
 struct Bf16Tile {
-  static constexpr int CH = D / 8;               // 16-byte chunks per K row
+  static constexpr int CH = D / 8;               // 16-byte chunks per K/V row
   static constexpr int KC = D / 16;              // k-steps of the QK MFMA
   static constexpr int DT = D / 32;              // 32-row d tiles of the PV MFMA
-  static constexpr int K_BYTES = BN * D * 2;     // one K block in LDS
-  static constexpr int V_BYTES = D * BN * 2;     // one V^T block in LDS
+  static constexpr int ROW = D * 2;              // bytes per K/V row in LDS
+  static constexpr int K_BYTES = BN * ROW;       // one K block in LDS
+  static constexpr int V_BYTES = BN * ROW;       // one V block in LDS
   static constexpr int BUF = K_BYTES + V_BYTES;  // one stage
-  static constexpr int KU = BN * CH / kAttnThreads;  // K 16-byte loads per thread
-  static constexpr int VQ = 16 * CH;                 // (4 keys x 16 bytes) V units per block
+  static constexpr int KU = BN * CH / kAttnThreads;  // 16-byte loads per thread, K (and V)
 };
 
-// Chunk swizzle of a K row so 16 consecutive rows hit 16 distinct bank groups.
+// K row chunk swizzle: the 16 rows one MFMA read touches land in 16 distinct
+// 16-byte bank groups.
 template <int CH>
 __device__ __forceinline__ int k_swz(int row) {
   return CH % 16 == 0 ? (row & 15) : ((row >> 1) & 7);
 }
-// Chunk swizzle of a V^T row (128 bytes = 8 chunks).
-__device__ __forceinline__ int v_swz(int d) { return (d >> 1) & 7; }
-
-// LDS position of key `kq*4` inside a 64-key V^T row: bits 2 and 3 of the key
-// swapped, so that the 8 keys one lane feeds to a PV MFMA are contiguous.
-__device__ __forceinline__ int v_pos4(int kq) {
-  return ((kq & 0xC) | ((kq & 1) << 1) | ((kq >> 1) & 1)) * 4;
+// V row swizzle, in 32-byte chunk pairs: the 4 consecutive rows one
+// ds_read_b64_tr_b16 group reads land in 4 distinct pairs.
+template <int CH>
+__device__ __forceinline__ int v_swz(int row) {
+  return CH % 16 == 0 ? ((row & 7) << 1) : ((row & 3) << 1);
 }
-
-__device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
 template <int D>
 __global__ __launch_bounds__(kAttnThreads, 2) void prefill_bf16_kernel(
@@ -72,7 +78,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_bf16_kernel(
   __shared__ __attribute__((aligned(16))) unsigned char lds[2 * T::BUF];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps per-wave values in SGPRs
   const int l32 = lane & 31, hf = lane >> 5;
 
   // ---- work decomposition (consecutive workgroups share the q tile and walk
@@ -89,18 +96,19 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_bf16_kernel(
   const int wg_row0 = qt * kRowsPerWave * rs;
   const int row0 = wg_row0 + (wave / hp) * kRowsPerWave;
   const int q = row0 + l32;
-  const int qc = q < Sq ? q : Sq - 1;
 
   const size_t q_base = (size_t)(b * Hq + head) * Sq * D;
   const size_t kv_base = (size_t)(b * Hkv + kvh) * Sk * D;
-  const uint16_t* Kb = Kg + kv_base;
-  const uint16_t* Vb = Vg + kv_base;
+  // Rows past Sq (queries) or Sk (keys) read as zeros.
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc(Qg + q_base, (uint32_t)Sq * D * 2);
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(Kg + kv_base, (uint32_t)Sk * D * 2);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(Vg + kv_base, (uint32_t)Sk * D * 2);
 
   // ---- Q as the B operand: lane (query l32, half hf) holds d = 16kc + 8hf .. +8 ----
   bf16x8 qreg[T::KC];
 #pragma unroll
   for (int kc = 0; kc < T::KC; ++kc)
-    qreg[kc] = __builtin_bit_cast(bf16x8, ld16(Qg + q_base + (size_t)qc * D + kc * 16 + hf * 8));
+    qreg[kc] = __builtin_bit_cast(bf16x8, buf_ld16(qr, (uint32_t)(q * D + kc * 16 + hf * 8) * 2));
 
   // ---- key range ----
   int wg_row_end = wg_row0 + kRowsPerWave * rs;
@@ -108,30 +116,26 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_bf16_kernel(
   const bool cmask = causal && Sq > 1;
   const int n_keys = cmask ? (wg_row_end < Sk ? wg_row_end : Sk) : Sk;
   const int nblk = (n_keys + BN - 1) / BN;
+  // Blocks [0, n_full) need no mask for any row of the workgroup.
+  int n_full = Sk / BN;
+  if (cmask) {
+    const int diag = (wg_row0 + 1) / BN;  // blocks with j0 + BN - 1 <= wg_row0
+    n_full = n_full < diag ? n_full : diag;
+  }
+  if (n_full > nblk) n_full = nblk;
   const int wave_row_last = row0 + kRowsPerWave - 1;
 
-  u32x4 kst[T::KU];
-  u32x4 vst[4];
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
-
+  // ---- global -> LDS staging: thread t moves 16-byte chunks u = t + 256 r ----
+  u32x4 kst[T::KU], vst[T::KU];
   auto load_block = [&](int j0) {
 #pragma unroll
     for (int r = 0; r < T::KU; ++r) {
       const int u = tid + kAttnThreads * r;
-      const int key = u / T::CH, ch = u % T::CH;
-      const int j = j0 + key;
-      kst[r] = j < Sk ? ld16(Kb + (size_t)j * D + ch * 8) : zero4;
-    }
-    if (tid < T::VQ) {
-      const int kq = tid / T::CH, ch = tid % T::CH;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int j = j0 + kq * 4 + jj;
-        vst[jj] = j < Sk ? ld16(Vb + (size_t)j * D + ch * 8) : zero4;
-      }
+      const uint32_t off = (uint32_t)((j0 + u / T::CH) * D + (u % T::CH) * 8) * 2;
+      kst[r] = buf_ld16(kr, off);
+      vst[r] = buf_ld16(vr, off);
     }
   };
-
   auto store_block = [&](int buf) {
     unsigned char* kl = lds + buf * T::BUF;
     unsigned char* vl = kl + T::K_BYTES;
@@ -139,126 +143,129 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_bf16_kernel(
     for (int r = 0; r < T::KU; ++r) {
       const int u = tid + kAttnThreads * r;
       const int key = u / T::CH, ch = u % T::CH;
-      *reinterpret_cast<u32x4*>(kl + key * (D * 2) + ((ch ^ k_swz<T::CH>(key)) << 4)) = kst[r];
-    }
-    if (tid < T::VQ) {
-      const int kq = tid / T::CH, ch = tid % T::CH;
-      const int pos = v_pos4(kq);
-      const int cc = pos >> 3, half = (pos >> 2) & 1;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1;
-        uint32_t lo, hi;
-        if (e & 1) {
-          lo = (vst[0][w] >> 16) | (vst[1][w] & 0xffff0000u);
-          hi = (vst[2][w] >> 16) | (vst[3][w] & 0xffff0000u);
-        } else {
-          lo = (vst[0][w] & 0xffffu) | (vst[1][w] << 16);
-          hi = (vst[2][w] & 0xffffu) | (vst[3][w] << 16);
-        }
-        const int d = ch * 8 + e;
-        const u32x2 val = {lo, hi};
-        *reinterpret_cast<u32x2*>(vl + d * (BN * 2) + ((cc ^ v_swz(d)) << 4) + half * 8) = val;
-      }
+      *reinterpret_cast<u32x4*>(kl + key * T::ROW + ((ch ^ k_swz<T::CH>(key)) << 4)) = kst[r];
+      *reinterpret_cast<u32x4*>(vl + key * T::ROW + ((ch ^ v_swz<T::CH>(key)) << 4)) = vst[r];
     }
   };
+
+  // ---- per-lane constants of the transposed V read (ds_read_b64_tr_b16) ----
+  // In each 16-lane group, source lane s points at row base + s/4, columns
+  // c0 + 4(s%4) .. +4; lane i then receives column c0 + i of those 4 rows.
+  // Lane (d = l32, hf) needs keys 16u + 4hf + 0..3 and 16u + 8 + 4hf + 0..3 of
+  // column d; with groups 0/1 = (hf 0, d 0-15 / 16-31) and 2/3 = (hf 1, ...):
+  const int grp16 = lane >> 4, s16 = lane & 15;
+  const int v_col = 16 * (grp16 & 1) + 4 * (s16 & 3);  // + 32 dt
+  const int v_row = 4 * (grp16 >> 1) + (s16 >> 2);     // + 32 t + 16 u (+ 8 for the upper 4 keys)
 
   f32x16 acc[T::DT];
 #pragma unroll
   for (int i = 0; i < T::DT; ++i) acc[i] = f32x16{};
-  float m_run = kNegInf, l_run = 0.f;
+  float m_ref = kNegInf, l_run = 0.f;
 
-  if (nblk > 0) {
-    load_block(0);
-    store_block(0);
-  }
-  __syncthreads();
-
-  for (int jb = 0; jb < nblk; ++jb) {
+  auto compute = [&](int jb, auto masked) {
+    constexpr bool MASK = decltype(masked)::value;
     const int j0 = jb * BN;
-    const bool has_next = jb + 1 < nblk;
-    if (has_next) load_block(j0 + BN);
+    const unsigned char* kl = lds + (jb & 1) * T::BUF;
+    const unsigned char* vl = kl + T::K_BYTES;
 
-    // A wavefront whose rows all precede this block sees none of it.
-    const bool active = !(cmask && j0 > wave_row_last);
-    if (active) {
-      const unsigned char* kl = lds + (jb & 1) * T::BUF;
-      const unsigned char* vl = kl + T::K_BYTES;
-
-      // ---- S^T = K Q^T : two 32-key sub-tiles ----
-      f32x16 s[2] = {f32x16{}, f32x16{}};
+    // ---- S^T = K Q^T : two 32-key sub-tiles ----
+    f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-      for (int kc = 0; kc < T::KC; ++kc) {
+    for (int kc = 0; kc < T::KC; ++kc) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int key = 32 * t + l32;
-          const int ch = 2 * kc + hf;
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kl + key * (D * 2) + ((ch ^ k_swz<T::CH>(key)) << 4));
-          s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kc], s[t], 0, 0, 0);
-        }
+      for (int t = 0; t < 2; ++t) {
+        const int key = 32 * t + l32;
+        const int ch = 2 * kc + hf;
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kl + key * T::ROW + ((ch ^ k_swz<T::CH>(key)) << 4));
+        s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kc], s[t], 0, 0, 0);
       }
+    }
 
-      // ---- mask: keys past the end, keys after the query (causal) ----
-      const bool need_mask = (j0 + BN > Sk) || (cmask && j0 + BN - 1 > row0);
-      if (need_mask) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kidx = j0 + 32 * t + 8 * (r >> 2) + 4 * hf + (r & 3);
-            const bool ok = kidx < Sk && (!cmask || kidx <= q);
-            s[t][r] = ok ? s[t][r] : kNegInf;
-          }
-      }
-
-      // ---- online softmax (log2 domain) ----
-      float mx = s[0][0];
+    // ---- mask: keys past the end, keys after the query (causal) ----
+    if (MASK) {
+      // key j0 + 4hf + o is visible iff o < lim, o = 32t + 8(r/4) + r%4
+      int lim = cmask ? (q + 1 < Sk ? q + 1 : Sk) : Sk;
+      lim -= j0 + 4 * hf;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx * c);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = exp2_fast(m_run - m_use);
-      // P is rounded to bf16 once; the same rounded values feed the PV MFMA and
-      // the denominator, so the weights of a row sum to exactly one.
-      bf16x8 pb[2][2];
-      float rsum = 0.f;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          float p[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) p[i] = exp2_fast(fmaf(s[t][8 * u + i], c, -m_use));
-          pb[t][u] = pack_bf16x8_sum(p, rsum);
-        }
-      l_run = l_run * alpha + rsum;
-      m_run = m_new;
-      if (__ballot(alpha != 1.0f)) {
-#pragma unroll
-        for (int i = 0; i < T::DT; ++i) acc[i] *= alpha;
-      }
-
-      // ---- O^T += V^T P^T ----
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int cc = 4 * t + 2 * u + hf;
-#pragma unroll
-          for (int dt = 0; dt < T::DT; ++dt) {
-            const int d = 32 * dt + l32;
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(vl + d * (BN * 2) + ((cc ^ v_swz(d)) << 4));
-            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[t][u], acc[dt], 0, 0, 0);
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int o = 32 * t + 8 * (r >> 2) + (r & 3);
+          s[t][r] = o < lim ? s[t][r] : kNegInf;
         }
     }
 
+    // ---- online softmax (log2 domain) ----
+    float mx = s[0][0];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+    // Move the reference only when the max outgrows it by more than 2^8.
+    if (__ballot(mx > m_ref + kRescaleSlack)) {
+      const float m_new = fmaxf(m_ref, mx);
+      if (m_new != kNegInf) {  // a row with no visible key yet keeps the empty state
+        const float alpha = exp2_fast(m_ref - m_new);  // 0 on the first visible block
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < T::DT; ++i) acc[i] *= alpha;
+        m_ref = m_new;
+      }
+    }
+    const float m_use = m_ref == kNegInf ? 0.f : m_ref;
+
+    // P is rounded to bf16 once; the same rounded values feed the PV MFMA and
+    // the denominator, so the weights of a row sum to exactly one.
+    bf16x8 pb[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        float p[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p[i] = exp2_fast(fmaf(s[t][8 * u + i], c, -m_use));
+        pb[t][u] = pack_bf16x8_sum(p, l_run);
+      }
+
+    // ---- O^T += V^T P^T: A operand = 8 keys of column d, two transposed reads ----
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int dt = 0; dt < T::DT; ++dt) {
+          const int col = 32 * dt + v_col;
+          const int r0 = 32 * t + 16 * u + v_row, r1 = r0 + 8;
+          const unsigned char* p0 = vl + r0 * T::ROW + (((col >> 3) ^ v_swz<T::CH>(r0)) << 4) + (col & 7) * 2;
+          const unsigned char* p1 = vl + r1 * T::ROW + (((col >> 3) ^ v_swz<T::CH>(r1)) << 4) + (col & 7) * 2;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
+          const i16x8 v8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v8), pb[t][u], acc[dt], 0,
+                                                            0, 0);
+        }
+      }
+  };
+
+  // nblk >= 1: every query row sees at least key 0.
+  load_block(0);
+  store_block(0);
+  wait_vmem();
+  __syncthreads();
+
+  auto step = [&](int jb, auto masked) {
+    const bool has_next = jb + 1 < nblk;
+    if (has_next) load_block((jb + 1) * BN);
+    // A wavefront whose rows all precede this block sees none of it.
+    if (!decltype(masked)::value || !(cmask && jb * BN > wave_row_last)) compute(jb, masked);
     if (has_next) store_block((jb + 1) & 1);
+    wait_vmem();
     __syncthreads();
-  }
+  };
+  int jb = 0;
+  for (; jb < n_full; ++jb) step(jb, std::false_type{});
+  for (; jb < nblk; ++jb) step(jb, std::true_type{});
 
   // ---- epilogue: O = acc / l, bf16 round-to-nearest-even ----
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);

@@ -38,8 +38,6 @@ __device__ __forceinline__ int k_swz(int row) {
   return CH % 16 == 0 ? (row & 15) : ((row >> 1) & 7);
 }
 
-__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
-
 template <int DP>
 __global__ __launch_bounds__(kAttnThreads, 2) void prefill_f32_kernel(
     const float* __restrict__ Qg, const float* __restrict__ Kg, const float* __restrict__ Vg, float* __restrict__ Og,
@@ -49,7 +47,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_f32_kernel(
   __shared__ __attribute__((aligned(16))) unsigned char lds[2 * T::BUF];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps per-wave values in SGPRs
   const int l32 = lane & 31, hf = lane >> 5;
 
   int qt = blockIdx.x / units_per_tile;
@@ -64,19 +63,21 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_f32_kernel(
   const int wg_row0 = qt * kRowsPerWave * rs;
   const int row0 = wg_row0 + (wave / hp) * kRowsPerWave;
   const int q = row0 + l32;
-  const int qc = q < Sq ? q : Sq - 1;
 
   const size_t q_base = (size_t)(b * Hq + head) * Sq * d;
   const size_t kv_base = (size_t)(b * Hkv + kvh) * Sk * d;
-  const float* Kb = Kg + kv_base;
-  const float* Vb = Vg + kv_base;
+  // Rows past Sq / Sk read as zeros; padded columns (d <= col < DP) are zeroed by a select.
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc(Qg + q_base, (uint32_t)Sq * d * 4);
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(Kg + kv_base, (uint32_t)Sk * d * 4);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(Vg + kv_base, (uint32_t)Sk * d * 4);
 
   // Q as the B operand: lane (query l32, half hf) holds d = hf*DP/2 + j.
   float qv[T::HALF];
 #pragma unroll
   for (int j = 0; j < T::HALF; j += 4) {
     const int col = hf * T::HALF + j;
-    const f32x4 x = col < d ? ld4(Qg + q_base + (size_t)qc * d + col) : f32x4{};
+    f32x4 x = buf_ld16f(qr, (uint32_t)(q * d + col) * 4);
+    if (col >= d) x = f32x4{};
     qv[j] = x.x;
     qv[j + 1] = x.y;
     qv[j + 2] = x.z;
@@ -96,10 +97,13 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_f32_kernel(
     for (int r = 0; r < T::PER_T; ++r) {
       const int u = tid + kAttnThreads * r;
       const int key = u / T::CH, col = (u % T::CH) * 4;
-      const int j = j0 + key;
-      const bool ok = u < T::UNITS && j < Sk && col < d;
-      kst[r] = ok ? ld4(Kb + (size_t)j * d + col) : f32x4{};
-      vst[r] = ok ? ld4(Vb + (size_t)j * d + col) : f32x4{};
+      const uint32_t off = (uint32_t)((j0 + key) * d + col) * 4;
+      kst[r] = buf_ld16f(kr, off);
+      vst[r] = buf_ld16f(vr, off);
+      if (col >= d) {
+        kst[r] = f32x4{};
+        vst[r] = f32x4{};
+      }
     }
   };
   auto store_block = [&](int buf) {
@@ -121,10 +125,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_f32_kernel(
   for (int i = 0; i < T::DT; ++i) acc[i] = f32x16{};
   float m_run = kNegInf, l_run = 0.f;
 
-  if (nblk > 0) {
-    load_block(0);
-    store_block(0);
-  }
+  // nblk >= 1: every query row sees at least key 0.
+  load_block(0);
+  store_block(0);
+  wait_vmem();
   __syncthreads();
 
   for (int jb = 0; jb < nblk; ++jb) {
@@ -193,6 +197,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_f32_kernel(
     }
 
     if (has_next) store_block((jb + 1) & 1);
+    wait_vmem();
     __syncthreads();
   }
 
