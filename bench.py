@@ -10,8 +10,9 @@ softmax (GB/s, 2 reads + 1 write), the fp32 4096^2 attention (TFLOP/s) and the
 two small latency cases (microseconds).
 
 Inputs are seeded synthetic tensors (``synth``), generated on the host and
-copied to HBM before timing.  Kernel durations come from HIP events recorded
-on the stream the kernels run on, around every call in the timed region.
+copied to HBM before timing.  Durations come from one HIP event pair recorded
+on the stream the kernels run on, around the whole timed region of
+back-to-back calls, divided by the number of calls.
 
 ``--gpus N`` with N > 1 exits: this build runs on one GPU.
 Prints one JSON line on stdout.
@@ -29,6 +30,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 MFMA / vector
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PREWARM_S = 0.5            # untimed run before the warm-up steps, so clocks are up
 METRIC = "attn fwd TFLOP/s (causal-adjusted) & softmax/decode GB/s, % of MI355X peak"
 KERNEL_SOURCES = {
     "prefill_bf16_kernel": "online_softmax_02_amd/csrc/attn_prefill_bf16.hip",
@@ -72,21 +74,33 @@ def traffic_for(kernel: str):
 
 
 def timed(torch, fn, steps, warmup):
-    """Warm up, then time `steps` calls; returns (wall seconds, per-call ms list)."""
+    """Warm up, then time `steps` back-to-back calls.
+
+    The call first runs untimed for PREWARM_S seconds (GPU clocks ramp up
+    over the first few hundred milliseconds), then `warmup` times.
+    One HIP event pair on the launch stream brackets the whole timed region, so
+    the host keeps the GPU queue full (per-call event pairs would count the
+    host's argument marshalling whenever the GPU catches up).  Returns
+    (wall seconds, mean GPU ms per call)."""
+    # Bring the GPU clocks up first: run the call for ~0.5 s (untimed).
+    t_end = time.perf_counter() + PREWARM_S
+    while time.perf_counter() < t_end:
+        for _ in range(4):
+            fn(0)
+        torch.cuda.synchronize()
     for i in range(warmup):
         fn(i)
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    start.record(stream)
     for i in range(steps):
-        ev[i][0].record(stream)
         fn(warmup + i)
-        ev[i][1].record(stream)
+    end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall, [a.elapsed_time(b) for a, b in ev]
+    return wall, start.elapsed_time(end) / steps
 
 
 def to_dev(a):
@@ -116,8 +130,7 @@ def bench_prefill(torch, osx, args):
     w = synth.WORKLOADS["gqa_prefill_bf16"]
     t, q, k, v = attn_tensors(torch, w)
     out = torch.empty_like(q)
-    wall, per = timed(torch, lambda i: osx.attn_fwd(q, k, v, causal=True, out=out), args.steps, args.warmup)
-    kern_ms = sum(per) / len(per)
+    wall, kern_ms = timed(torch, lambda i: osx.attn_fwd(q, k, v, causal=True, out=out), args.steps, args.warmup)
     tflops = w.flops() / (kern_ms * 1e-3) / 1e12
     res = {"wall_s": wall, "ms_per_step": wall / args.steps * 1e3, "kernel_ms": kern_ms, "tflops": tflops,
            "roofline": roofline("mfma", tflops, PEAK_BF16_TFLOPS, "TFLOP/s", traffic_for("prefill_bf16_kernel"))}
@@ -131,8 +144,7 @@ def bench_decode(torch, osx, args):
     out = torch.empty_like(q)
     ws = torch.empty(osx.attn_fwd_workspace(osx.OSX_BF16, w.batch, w.heads_q, w.heads_kv, 1, w.seq_k, w.head_dim),
                      dtype=torch.uint8, device="cuda")
-    wall, per = timed(torch, lambda i: osx.attn_fwd(q, k, v, out=out, workspace=ws), args.steps, args.warmup)
-    ms = sum(per) / len(per)
+    wall, ms = timed(torch, lambda i: osx.attn_fwd(q, k, v, out=out, workspace=ws), args.steps, args.warmup)
     gbs = w.bytes() / (ms * 1e-3) / 1e9
     return {"workload": w.name, "unit": "GB/s", "value": round(gbs, 1), "call_us": round(ms * 1e3, 2),
             "bytes_per_call": w.bytes(),
@@ -147,9 +159,8 @@ def bench_softmax(torch, osx, args):
     xs = [x.clone() for _ in range(5)]
     ys = [torch.empty_like(x) for _ in range(5)]
     ws = torch.empty(osx.softmax_rows_workspace(w.rows, w.cols), dtype=torch.uint8, device="cuda")
-    wall, per = timed(torch, lambda i: osx.softmax_rows(xs[i % 5], out=ys[i % 5], workspace=ws), args.steps,
-                      args.warmup)
-    ms = sum(per) / len(per)
+    wall, ms = timed(torch, lambda i: osx.softmax_rows(xs[i % 5], out=ys[i % 5], workspace=ws), args.steps,
+                     args.warmup)
     gbs = w.bytes() / (ms * 1e-3) / 1e9
     return {"workload": w.name, "unit": "GB/s", "value": round(gbs, 1), "call_us": round(ms * 1e3, 2),
             "bytes_per_call": w.bytes(),
@@ -161,8 +172,7 @@ def bench_f32(torch, osx, args):
     w = synth.WORKLOADS["attn_f32_4k_d128"]
     _, q, k, v = attn_tensors(torch, w)
     out = torch.empty_like(q)
-    wall, per = timed(torch, lambda i: osx.attn_fwd(q, k, v, out=out), args.steps, args.warmup)
-    ms = sum(per) / len(per)
+    wall, ms = timed(torch, lambda i: osx.attn_fwd(q, k, v, out=out), args.steps, args.warmup)
     tf = w.flops() / (ms * 1e-3) / 1e12
     return {"workload": w.name, "unit": "TFLOP/s", "value": round(tf, 2), "call_us": round(ms * 1e3, 2),
             "roofline": roofline("mfma", tf, PEAK_F32_TFLOPS, "TFLOP/s", traffic_for("prefill_f32_kernel"))}
@@ -174,14 +184,14 @@ def bench_small(torch, osx, args):
     w = synth.WORKLOADS["attn_f32_m64_n100_d48"]
     _, q, k, v = attn_tensors(torch, w)
     out = torch.empty_like(q)
-    _, per = timed(torch, lambda i: osx.attn_fwd(q, k, v, out=out), args.steps, args.warmup)
-    res[w.name] = {"unit": "us", "value": round(1e3 * sum(per) / len(per), 2),
+    _, ms = timed(torch, lambda i: osx.attn_fwd(q, k, v, out=out), args.steps, args.warmup)
+    res[w.name] = {"unit": "us", "value": round(1e3 * ms, 2),
                    "note": "launch-latency bound; roofline fraction not meaningful"}
     w = synth.WORKLOADS["softmax_4x200"]
     x = to_dev(synth.softmax_inputs(w))
     y = torch.empty_like(x)
-    _, per = timed(torch, lambda i: osx.softmax_rows(x, out=y), args.steps, args.warmup)
-    res[w.name] = {"unit": "us", "value": round(1e3 * sum(per) / len(per), 2),
+    _, ms = timed(torch, lambda i: osx.softmax_rows(x, out=y), args.steps, args.warmup)
+    res[w.name] = {"unit": "us", "value": round(1e3 * ms, 2),
                    "note": "launch-latency bound; roofline fraction not meaningful"}
     return res
 

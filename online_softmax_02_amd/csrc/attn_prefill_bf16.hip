@@ -12,8 +12,11 @@
 //  * A workgroup is 4 wavefronts.  Each wavefront owns 32 query rows of one
 //    query head; the workgroup's wavefronts share one KV head (GQA: query head h
 //    reads KV head h / G), either 4 heads x 32 rows, 2 x 64 or 1 x 128.
-//  * K and V blocks of 64 keys are staged through LDS (double buffered, one
-//    barrier per block) with 16-byte buffer loads; rows past the end read as 0.
+//  * K and V blocks of 64 keys are staged through LDS (two buffers each, one
+//    barrier per block) with 16-byte direct-to-LDS buffer loads (no register
+//    staging); rows past the end read as 0.
+//    K runs one block ahead: the QK MFMAs of block j+1 are issued while the
+//    exponentials of block j run on the VALU, then block j's PV MFMAs follow.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //    a lane then holds 16 scores of ONE query, so the row max and row sum are
 //    lane-local (plus one cross-half exchange for the max per block) and the
@@ -52,7 +55,6 @@ struct Bf16Tile {
   static constexpr int ROW = D * 2;              // bytes per K/V row in LDS
   static constexpr int K_BYTES = BN * ROW;       // one K block in LDS
   static constexpr int V_BYTES = BN * ROW;       // one V block in LDS
-  static constexpr int BUF = K_BYTES + V_BYTES;  // one stage
   static constexpr int KU = BN * CH / kAttnThreads;  // 16-byte loads per thread, K (and V)
 };
 
@@ -75,7 +77,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_bf16_kernel(
     uint16_t* __restrict__ Og, int Hq, int Hkv, int Sq, int Sk, int causal, float c, int hp, int n_hgroups,
     int n_qtiles, int units_per_tile) {
   using T = Bf16Tile<D>;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * T::BUF];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * T::K_BYTES + 2 * T::V_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -125,28 +127,29 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_bf16_kernel(
   if (n_full > nblk) n_full = nblk;
   const int wave_row_last = row0 + kRowsPerWave - 1;
 
-  // ---- global -> LDS staging: thread t moves 16-byte chunks u = t + 256 r ----
-  u32x4 kst[T::KU], vst[T::KU];
-  auto load_block = [&](int j0) {
+  // ---- global -> LDS staging with buffer_load_dwordx4 ... lds ----
+  // LDS holds two K buffers and two V buffers.  K runs one block ahead of V:
+  // while block jb's softmax and PV run, the QK of block jb+1 is issued.
+  // A direct-to-LDS load writes lane i's 16 bytes at M0 + 16 i, so each lane
+  // fetches the global chunk that belongs in its (swizzled) LDS slot.
+  // One wavefront instruction fills LDS_ROWS rows; the block needs LDS_STEPS
+  // such instructions, spread over the 4 wavefronts.
+  constexpr int LDS_ROWS = 64 / T::CH;                 // rows per 1 KiB instruction
+  constexpr int LDS_STEPS = BN / LDS_ROWS / kAttnWaves;  // instructions per wavefront per block
+  const int dma_row = lane / T::CH, dma_chunk = lane % T::CH;
+  auto dma_block = [&](__amdgpu_buffer_rsrc_t rsrc, int j0, int lds_off, bool is_v) {
 #pragma unroll
-    for (int r = 0; r < T::KU; ++r) {
-      const int u = tid + kAttnThreads * r;
-      const uint32_t off = (uint32_t)((j0 + u / T::CH) * D + (u % T::CH) * 8) * 2;
-      kst[r] = buf_ld16(kr, off);
-      vst[r] = buf_ld16(vr, off);
+    for (int r = 0; r < LDS_STEPS; ++r) {
+      const int inst = r * kAttnWaves + wave;  // uniform
+      const int row = inst * LDS_ROWS + dma_row;
+      const int src_chunk = dma_chunk ^ (is_v ? v_swz<T::CH>(row) : k_swz<T::CH>(row));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (__attribute__((address_space(3))) void*)(lds + lds_off + inst * 1024), 16,
+          (int)((uint32_t)((j0 + row) * D + src_chunk * 8) * 2), 0, 0, 0);
     }
   };
-  auto store_block = [&](int buf) {
-    unsigned char* kl = lds + buf * T::BUF;
-    unsigned char* vl = kl + T::K_BYTES;
-#pragma unroll
-    for (int r = 0; r < T::KU; ++r) {
-      const int u = tid + kAttnThreads * r;
-      const int key = u / T::CH, ch = u % T::CH;
-      *reinterpret_cast<u32x4*>(kl + key * T::ROW + ((ch ^ k_swz<T::CH>(key)) << 4)) = kst[r];
-      *reinterpret_cast<u32x4*>(vl + key * T::ROW + ((ch ^ v_swz<T::CH>(key)) << 4)) = vst[r];
-    }
-  };
+  auto load_k = [&](int j0, int buf) { dma_block(kr, j0, buf * T::K_BYTES, false); };
+  auto load_v = [&](int j0, int buf) { dma_block(vr, j0, 2 * T::K_BYTES + buf * T::V_BYTES, true); };
 
   // ---- per-lane constants of the transposed V read (ds_read_b64_tr_b16) ----
   // In each 16-lane group, source lane s points at row base + s/4, columns
@@ -162,14 +165,11 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_bf16_kernel(
   for (int i = 0; i < T::DT; ++i) acc[i] = f32x16{};
   float m_ref = kNegInf, l_run = 0.f;
 
-  auto compute = [&](int jb, auto masked) {
-    constexpr bool MASK = decltype(masked)::value;
-    const int j0 = jb * BN;
-    const unsigned char* kl = lds + (jb & 1) * T::BUF;
-    const unsigned char* vl = kl + T::K_BYTES;
-
-    // ---- S^T = K Q^T : two 32-key sub-tiles ----
-    f32x16 s[2] = {f32x16{}, f32x16{}};
+  // S^T = K Q^T for the block in K buffer `buf`: two 32-key sub-tiles.
+  auto qk = [&](int buf, f32x16 (&s)[2]) {
+    const unsigned char* kl = lds + buf * T::K_BYTES;
+    s[0] = f32x16{};
+    s[1] = f32x16{};
 #pragma unroll
     for (int kc = 0; kc < T::KC; ++kc) {
 #pragma unroll
@@ -180,6 +180,16 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_bf16_kernel(
         s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kc], s[t], 0, 0, 0);
       }
     }
+  };
+
+  f32x16 s_cur[2], s_nxt[2];
+
+  // Softmax of block jb (scores in s_cur), QK of block jb+1 into s_nxt, then
+  // O^T += V^T P^T for block jb.
+  auto compute = [&](int jb, auto masked) {
+    constexpr bool MASK = decltype(masked)::value;
+    const int j0 = jb * BN;
+    f32x16(&s)[2] = s_cur;
 
     // ---- mask: keys past the end, keys after the query (causal) ----
     if (MASK) {
@@ -215,6 +225,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_bf16_kernel(
     }
     const float m_use = m_ref == kNegInf ? 0.f : m_ref;
 
+    // ---- next block's scores (MFMA), overlapping the exponentials below (VALU).
+    // On the last block this reads the other K buffer's stale contents and the
+    // result is discarded; computing it unconditionally keeps the loop body
+    // branch-free. ----
+    qk((jb + 1) & 1, s_nxt);
+
     // P is rounded to bf16 once; the same rounded values feed the PV MFMA and
     // the denominator, so the weights of a row sum to exactly one.
     bf16x8 pb[2][2];
@@ -229,6 +245,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_bf16_kernel(
       }
 
     // ---- O^T += V^T P^T: A operand = 8 keys of column d, two transposed reads ----
+    const unsigned char* vl = lds + 2 * T::K_BYTES + (jb & 1) * T::V_BYTES;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -248,18 +265,31 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_bf16_kernel(
       }
   };
 
+  // ---- prologue: K0, V0, K1 in LDS; scores of block 0 ----
   // nblk >= 1: every query row sees at least key 0.
-  load_block(0);
-  store_block(0);
+  load_k(0, 0);
+  load_v(0, 0);
+  if (nblk > 1) load_k(BN, 1);
   wait_vmem();
   __syncthreads();
+  qk(0, s_cur);
 
+  // Iteration jb: streams K[jb+2] into the K buffer block jb used and V[jb+1]
+  // into the V buffer block jb-1 used (both free since the last barrier),
+  // then runs block jb.
   auto step = [&](int jb, auto masked) {
-    const bool has_next = jb + 1 < nblk;
-    if (has_next) load_block((jb + 1) * BN);
-    // A wavefront whose rows all precede this block sees none of it.
-    if (!decltype(masked)::value || !(cmask && jb * BN > wave_row_last)) compute(jb, masked);
-    if (has_next) store_block((jb + 1) & 1);
+    const bool next1 = jb + 1 < nblk, next2 = jb + 2 < nblk;
+    if (next2) load_k((jb + 2) * BN, jb & 1);
+    if (next1) load_v((jb + 1) * BN, (jb + 1) & 1);
+    // A wavefront whose rows all precede this block sees none of it (its
+    // scores for the next block are still computed: they may be visible).
+    if (!decltype(masked)::value || !(cmask && jb * BN > wave_row_last)) {
+      compute(jb, masked);
+    } else {
+      qk((jb + 1) & 1, s_nxt);
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) s_cur[t] = s_nxt[t];
     wait_vmem();
     __syncthreads();
   };
