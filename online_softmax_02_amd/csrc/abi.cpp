@@ -79,6 +79,18 @@ int plan_attn(int dtype, int batch, int heads_q, int heads_kv, int seq_q, int se
   p->heads_per_wg = hp;
   p->grid = (int64_t)batch * heads_kv * (groups / hp) * cdiv(seq_q, rows_per_wg);
   p->workspace_bytes = 0;
+  if (dtype == OSX_F32 && p->grid < osx::kSplitTargetWgs) {
+    // Too few row tiles to fill the GPU: split the keys (each slice at least
+    // kSplitMinBlocks blocks) and merge the slices' partial states afterwards.
+    int64_t splits = cdiv(osx::kSplitTargetWgs, p->grid);
+    const int64_t max_splits = seq_k / (osx::kF32BlockN * osx::kSplitMinBlocks);
+    if (splits > max_splits) splits = max_splits;
+    if (splits > 1) {
+      p->splits = (int)splits;
+      p->grid *= splits;
+      p->workspace_bytes = (size_t)((int64_t)batch * heads_q * seq_q * splits) * (size_t)(2 + head_dim) * sizeof(float);
+    }
+  }
   if (p->grid > 0x7fffffff) return fail(OSX_EUNSUPPORTED, "problem needs %lld workgroups", (long long)p->grid);
   return ok();
 }

@@ -12,6 +12,13 @@
 // score registers and V is read from a plain row-major LDS block.  The head
 // dimension d (a multiple of 4, at most 128) is padded with zeros up to DP,
 // a multiple of 32; padded columns are never stored.  Blocks are 32 keys.
+//
+// Few heads with long sequences (one 4096-row head gives 32 workgroups) would
+// leave most of the 256 CUs idle, so the keys can be split: workgroup
+// (tile, split) runs the recurrence over its slice of the keys and writes the
+// partial state (m, l, acc) of each row; a combine kernel merges the slices
+// with the rescaling rule of page "Softmax 算子的实现与优化", section Online
+// Softmax: m = max m_s, l = sum l_s 2^(m_s - m), O = sum acc_s 2^(m_s - m) / l.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -42,7 +49,7 @@ template <int DP>
 __global__ __launch_bounds__(kAttnThreads, 2) void prefill_f32_kernel(
     const float* __restrict__ Qg, const float* __restrict__ Kg, const float* __restrict__ Vg, float* __restrict__ Og,
     int Hq, int Hkv, int Sq, int Sk, int d, int causal, float c, int hp, int n_hgroups, int n_qtiles,
-    int units_per_tile) {
+    int units_per_tile, int splits, int keys_per_split, float* __restrict__ ws_ml, float* __restrict__ ws_acc) {
   using T = F32Tile<DP>;
   __shared__ __attribute__((aligned(16))) unsigned char lds[2 * T::BUF];
 
@@ -51,8 +58,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_f32_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps per-wave values in SGPRs
   const int l32 = lane & 31, hf = lane >> 5;
 
-  int qt = blockIdx.x / units_per_tile;
-  const int rem = blockIdx.x - qt * units_per_tile;
+  const int split = blockIdx.x % splits;
+  const int tile_id = blockIdx.x / splits;
+  int qt = tile_id / units_per_tile;
+  const int rem = tile_id - qt * units_per_tile;
   if (causal) qt = n_qtiles - 1 - qt;
   const int G = Hq / Hkv;
   const int b = rem / (Hkv * n_hgroups);
@@ -87,9 +96,14 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_f32_kernel(
   int wg_row_end = wg_row0 + kRowsPerWave * rs;
   if (wg_row_end > Sq) wg_row_end = Sq;
   const bool cmask = causal && Sq > 1;
-  const int n_keys = cmask ? (wg_row_end < Sk ? wg_row_end : Sk) : Sk;
+  int n_keys = cmask ? (wg_row_end < Sk ? wg_row_end : Sk) : Sk;
+  // This workgroup's slice of the keys: blocks [jb0, nblk).
+  const int k_begin = split * keys_per_split;
+  if (n_keys > k_begin + keys_per_split) n_keys = k_begin + keys_per_split;
+  const int jb0 = k_begin / BN;
   const int nblk = (n_keys + BN - 1) / BN;
   const int wave_row_last = row0 + kRowsPerWave - 1;
+  const size_t row_id = (size_t)(b * Hq + head) * Sq + q;  // partial-state row (split mode)
 
   f32x4 kst[T::PER_T], vst[T::PER_T];
   auto load_block = [&](int j0) {
@@ -125,13 +139,26 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_f32_kernel(
   for (int i = 0; i < T::DT; ++i) acc[i] = f32x16{};
   float m_run = kNegInf, l_run = 0.f;
 
-  // nblk >= 1: every query row sees at least key 0.
-  load_block(0);
-  store_block(0);
+  if (jb0 >= nblk) {
+    // Causal slice entirely after this tile's rows: an empty partial state.
+    if (q < Sq) {
+      if (hf == 0) {
+        ws_ml[(row_id * splits + split) * 2] = kNegInf;
+        ws_ml[(row_id * splits + split) * 2 + 1] = 0.f;
+      }
+      float* pa = ws_acc + (row_id * splits + split) * d;
+      for (int c0 = 4 * hf; c0 < d; c0 += 8) *reinterpret_cast<f32x4*>(pa + c0) = f32x4{};
+    }
+    return;
+  }
+
+  // Every slice that is not empty starts with a visible key for every row.
+  load_block(jb0 * BN);
+  store_block(jb0 & 1);
   wait_vmem();
   __syncthreads();
 
-  for (int jb = 0; jb < nblk; ++jb) {
+  for (int jb = jb0; jb < nblk; ++jb) {
     const int j0 = jb * BN;
     const bool has_next = jb + 1 < nblk;
     if (has_next) load_block(j0 + BN);
@@ -202,21 +229,63 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_f32_kernel(
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv = 1.0f / l_tot;
   if (q < Sq) {
-    float* op = Og + q_base + (size_t)q * d;
+    if (splits == 1) {
+      const float inv = 1.0f / l_tot;
+      float* op = Og + q_base + (size_t)q * d;
 #pragma unroll
-    for (int dt = 0; dt < T::DT; ++dt)
+      for (int dt = 0; dt < T::DT; ++dt)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * dt + 8 * g + 4 * hf;
-        if (d0 < d) {
-          const f32x4 w = {acc[dt][4 * g] * inv, acc[dt][4 * g + 1] * inv, acc[dt][4 * g + 2] * inv,
-                           acc[dt][4 * g + 3] * inv};
-          *reinterpret_cast<f32x4*>(op + d0) = w;
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * dt + 8 * g + 4 * hf;
+          if (d0 < d) {
+            const f32x4 w = {acc[dt][4 * g] * inv, acc[dt][4 * g + 1] * inv, acc[dt][4 * g + 2] * inv,
+                             acc[dt][4 * g + 3] * inv};
+            *reinterpret_cast<f32x4*>(op + d0) = w;
+          }
         }
+    } else {
+      // partial state of this slice: m (log2 domain), l and the unnormalised acc
+      if (hf == 0) {
+        ws_ml[(row_id * splits + split) * 2] = m_run;
+        ws_ml[(row_id * splits + split) * 2 + 1] = l_tot;
       }
+      float* pa = ws_acc + (row_id * splits + split) * d;
+#pragma unroll
+      for (int dt = 0; dt < T::DT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * dt + 8 * g + 4 * hf;
+          if (d0 < d)
+            *reinterpret_cast<f32x4*>(pa + d0) = f32x4{acc[dt][4 * g], acc[dt][4 * g + 1], acc[dt][4 * g + 2],
+                                                       acc[dt][4 * g + 3]};
+        }
+    }
   }
+}
+
+// Merge the key slices of each query row: one wavefront per row, lane c owns
+// columns c and c + 64.
+__global__ __launch_bounds__(256) void combine_f32_kernel(const float* __restrict__ ws_ml,
+                                                          const float* __restrict__ ws_acc, float* __restrict__ Og,
+                                                          int64_t rows, int splits, int d) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const float* ml = ws_ml + row * splits * 2;
+  float M = kNegInf;
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, ml[2 * s]);
+  float L = 0.f, a0 = 0.f, a1 = 0.f;
+  const float* pa = ws_acc + row * splits * d;
+  for (int s = 0; s < splits; ++s) {
+    const float w = exp2_fast(ml[2 * s] - M);  // 0 for an empty slice
+    L += ml[2 * s + 1] * w;
+    if (lane < d) a0 += pa[(int64_t)s * d + lane] * w;
+    if (lane + 64 < d) a1 += pa[(int64_t)s * d + lane + 64] * w;
+  }
+  const float inv = 1.0f / L;
+  if (lane < d) Og[row * d + lane] = a0 * inv;
+  if (lane + 64 < d) Og[row * d + lane + 64] = a1 * inv;
 }
 
 template <int DP>
@@ -227,10 +296,19 @@ hipError_t launch(const AttnArgs& a) {
   const int rows_per_wg = a.plan.block_m;
   const int n_qtiles = (a.seq_q + rows_per_wg - 1) / rows_per_wg;
   const int units_per_tile = a.batch * a.heads_kv * n_hgroups;
+  const int splits = a.plan.splits;
+  const int kps = splits == 1 ? a.seq_k : ((a.seq_k + splits - 1) / splits + BN - 1) / BN * BN;
+  const int64_t rows = (int64_t)a.batch * a.heads_q * a.seq_q;
+  float* ws_ml = static_cast<float*>(a.workspace);
+  float* ws_acc = splits == 1 ? nullptr : ws_ml + rows * splits * 2;
   hipLaunchKernelGGL(prefill_f32_kernel<DP>, dim3((unsigned)a.plan.grid), dim3(kAttnThreads), 0, a.stream,
                      static_cast<const float*>(a.q), static_cast<const float*>(a.k), static_cast<const float*>(a.v),
                      static_cast<float*>(a.o), a.heads_q, a.heads_kv, a.seq_q, a.seq_k, a.head_dim, a.causal, a.c, hp,
-                     n_hgroups, n_qtiles, units_per_tile);
+                     n_hgroups, n_qtiles, units_per_tile, splits, kps, ws_ml, ws_acc);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  hipLaunchKernelGGL(combine_f32_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, a.stream, ws_ml, ws_acc,
+                     static_cast<float*>(a.o), rows, splits, a.head_dim);
   return hipGetLastError();
 }
 

@@ -129,6 +129,44 @@ __device__ __forceinline__ void normalise(const float* __restrict__ x, float* __
   }
 }
 
+// A full chunk of kSoftmaxChunk elements, 16-byte loads: every thread issues
+// all of its kChunkVec loads before using any, so a workgroup keeps its whole
+// chunk in flight.  Thread state: its exact max, then the sum of
+// 2^((x - m) log2 e) over its values (the block-level merge is the rescaling
+// rule).  Pass 1 loads normally so x stays cached for pass 2; pass 2 is the
+// last use of x and streams y out with non-temporal accesses.
+constexpr int kChunkVec = (int)(kSoftmaxChunk / 4 / kThreads);  // float4 per thread per chunk
+
+__device__ __forceinline__ State scan_chunk(const float* __restrict__ xb) {
+  f32x4 v[kChunkVec];
+#pragma unroll
+  for (int i = 0; i < kChunkVec; ++i) v[i] = reinterpret_cast<const f32x4*>(xb)[threadIdx.x + i * kThreads];
+  float m = v[0].x;
+#pragma unroll
+  for (int i = 0; i < kChunkVec; ++i) m = fmaxf(fmaxf(m, fmaxf(v[i].x, v[i].y)), fmaxf(v[i].z, v[i].w));
+  float l = 0.f;
+#pragma unroll
+  for (int i = 0; i < kChunkVec; ++i)
+    l += (exp2_fast((v[i].x - m) * kLog2e) + exp2_fast((v[i].y - m) * kLog2e)) +
+         (exp2_fast((v[i].z - m) * kLog2e) + exp2_fast((v[i].w - m) * kLog2e));
+  return State{m, l};
+}
+
+__device__ __forceinline__ void normalise_chunk(const float* xb, float* yb, float m, float inv_l) {
+  f32x4 v[kChunkVec];
+#pragma unroll
+  for (int i = 0; i < kChunkVec; ++i) v[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(xb) + threadIdx.x + i * kThreads);
+#pragma unroll
+  for (int i = 0; i < kChunkVec; ++i) {
+    f32x4 r;
+    r.x = exp2_fast((v[i].x - m) * kLog2e) * inv_l;
+    r.y = exp2_fast((v[i].y - m) * kLog2e) * inv_l;
+    r.z = exp2_fast((v[i].z - m) * kLog2e) * inv_l;
+    r.w = exp2_fast((v[i].w - m) * kLog2e) * inv_l;
+    __builtin_nontemporal_store(r, reinterpret_cast<f32x4*>(yb) + threadIdx.x + i * kThreads);
+  }
+}
+
 // One workgroup per row: both passes.  x and y may be the same buffer.
 template <int VEC>
 __global__ __launch_bounds__(kThreads) void softmax_row_kernel(const float* x, float* y, int64_t cols) {
@@ -151,7 +189,8 @@ __global__ __launch_bounds__(kThreads) void softmax_split_pass1(const float* __r
   const int64_t ck = id - row * splits;
   const int64_t begin = ck * chunk;
   const int64_t end = begin + chunk < cols ? begin + chunk : cols;
-  State s = scan<VEC>(x + row * cols, begin, end);
+  State s = (VEC == 4 && end - begin == kSoftmaxChunk) ? scan_chunk(x + row * cols + begin)
+                                                        : scan<VEC>(x + row * cols, begin, end);
   s = block_merge(s, sm);
   if (threadIdx.x == 0) {
     part[2 * id] = s.m;
@@ -174,7 +213,10 @@ __global__ __launch_bounds__(kThreads) void softmax_split_pass2(const float* x, 
   s = block_merge(s, sm);
   const int64_t begin = ck * chunk;
   const int64_t end = begin + chunk < cols ? begin + chunk : cols;
-  normalise<VEC>(x + row * cols, y + row * cols, begin, end, s.m, 1.0f / s.l);
+  if (VEC == 4 && end - begin == kSoftmaxChunk)
+    normalise_chunk(x + row * cols + begin, y + row * cols + begin, s.m, 1.0f / s.l);
+  else
+    normalise<VEC>(x + row * cols, y + row * cols, begin, end, s.m, 1.0f / s.l);
 }
 
 }  // namespace

@@ -98,7 +98,10 @@ def test_plans_for_the_workloads():
     assert p["workspace_bytes"] == osx.attn_fwd_workspace(BF16, 64, 32, 8, 1, 8192, 128)
     assert p["workspace_bytes"] == 64 * 8 * p["splits"] * 4 * (2 + 128) * 4
     p = osx.attn_plan(F32, 1, 1, 1, 64, 100, 48)
-    assert p["kernel_name"] == "prefill_f32" and p["grid"] == 1
+    assert p["kernel_name"] == "prefill_f32" and p["grid"] == 1 and p["splits"] == 1
+    p = osx.attn_plan(F32, 1, 1, 1, 4096, 4096, 128)  # one head: the keys are split to fill the GPU
+    assert p["splits"] == 16 and p["grid"] == 32 * 16
+    assert p["workspace_bytes"] == 4096 * 16 * (2 + 128) * 4
     p = osx.attn_plan(BF16, 1, 40, 2, 1, 300, 128)  # 20 query heads per KV head: too many to pack
     assert p["kernel_name"] == "prefill_bf16"
     p = osx.softmax_rows_plan(4, 200)

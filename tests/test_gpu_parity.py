@@ -139,6 +139,8 @@ PREFILL_CASES = [
     ("f32", 1, 3, 3, 64, 64, 96, True),
     ("f32", 1, 1, 1, 1, 5, 32, True),
     ("f32", 1, 2, 2, 40, 1, 64, False),         # a single key
+    ("f32", 1, 1, 1, 600, 600, 64, True),       # key slices merged afterwards, some slices fully masked
+    ("f32", 1, 1, 1, 130, 1000, 128, False),    # key slices, ragged last slice
 ]
 
 
