@@ -64,11 +64,13 @@ template <int CH>
 __device__ __forceinline__ int k_swz(int row) {
   return CH % 16 == 0 ? (row & 15) : ((row >> 1) & 7);
 }
-// V row swizzle, in 32-byte chunk pairs: the 4 consecutive rows one
-// ds_read_b64_tr_b16 group reads land in 4 distinct pairs.
+// V row swizzle: a ds_read_b64_tr_b16 serves 32 lanes from 4 consecutive rows,
+// 64 bytes (4 chunks) of each; XOR-ing the chunk index with a multiple of 4
+// puts those 4 row segments in 4 distinct 64-byte bank groups (for 128-byte
+// rows, rows r and r+1 already sit in different bank halves).
 template <int CH>
 __device__ __forceinline__ int v_swz(int row) {
-  return CH % 16 == 0 ? ((row & 7) << 1) : ((row & 3) << 1);
+  return CH % 16 == 0 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
 }
 
 template <int D>
