@@ -83,7 +83,8 @@ int plan_attn(int dtype, int batch, int heads_q, int heads_kv, int seq_q, int se
     // Too few row tiles to fill the GPU: split the keys (each slice at least
     // kSplitMinBlocks blocks) and merge the slices' partial states afterwards.
     int64_t splits = cdiv(osx::kSplitTargetWgs, p->grid);
-    const int64_t max_splits = seq_k / (osx::kF32BlockN * osx::kSplitMinBlocks);
+    int64_t max_splits = seq_k / (osx::kF32BlockN * osx::kSplitMinBlocks);
+    if (max_splits > osx::kWaveSize) max_splits = osx::kWaveSize;  // the combine gives each slice one lane
     if (splits > max_splits) splits = max_splits;
     if (splits > 1) {
       p->splits = (int)splits;

@@ -79,7 +79,13 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_bf16_kernel(
     uint16_t* __restrict__ Og, int Hq, int Hkv, int Sq, int Sk, int causal, float c, int hp, int n_hgroups,
     int n_qtiles, int units_per_tile) {
   using T = Bf16Tile<D>;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * T::K_BYTES + 2 * T::V_BYTES];
+  // Four separate LDS objects (two K, two V buffers): the compiler can then
+  // tell a read of one buffer from a DMA into another and does not wait for
+  // the DMA before the read.
+  __shared__ __attribute__((aligned(16))) unsigned char lds_k0[T::K_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_k1[T::K_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_v0[T::V_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_v1[T::V_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -139,19 +145,22 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_bf16_kernel(
   constexpr int LDS_ROWS = 64 / T::CH;                 // rows per 1 KiB instruction
   constexpr int LDS_STEPS = BN / LDS_ROWS / kAttnWaves;  // instructions per wavefront per block
   const int dma_row = lane / T::CH, dma_chunk = lane % T::CH;
-  auto dma_block = [&](__amdgpu_buffer_rsrc_t rsrc, int j0, int lds_off, bool is_v) {
+  // The swizzle of a row depends only on its position within 16 rows, which
+  // the instruction index does not change: the lane's byte offset is fixed and
+  // the block and instruction offsets go into the scalar soffset.
+  const int dma_row0 = wave * LDS_ROWS + dma_row;
+  const int k_voff = (dma_row0 * D + ((dma_chunk ^ k_swz<T::CH>(dma_row0)) << 3)) * 2;
+  const int v_voff = (dma_row0 * D + ((dma_chunk ^ v_swz<T::CH>(dma_row0)) << 3)) * 2;
+  static_assert((kAttnWaves * LDS_ROWS) % 16 == 0, "row swizzle must repeat every instruction step");
+  auto dma_block = [&](__amdgpu_buffer_rsrc_t rsrc, int j0, unsigned char* dst, bool is_v) {
 #pragma unroll
     for (int r = 0; r < LDS_STEPS; ++r) {
       const int inst = r * kAttnWaves + wave;  // uniform
-      const int row = inst * LDS_ROWS + dma_row;
-      const int src_chunk = dma_chunk ^ (is_v ? v_swz<T::CH>(row) : k_swz<T::CH>(row));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsrc, (__attribute__((address_space(3))) void*)(lds + lds_off + inst * 1024), 16,
-          (int)((uint32_t)((j0 + row) * D + src_chunk * 8) * 2), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(dst + inst * 1024),
+                                               16, is_v ? v_voff : k_voff,
+                                               (j0 + r * kAttnWaves * LDS_ROWS) * D * 2, 0, 0);
     }
   };
-  auto load_k = [&](int j0, int buf) { dma_block(kr, j0, buf * T::K_BYTES, false); };
-  auto load_v = [&](int j0, int buf) { dma_block(vr, j0, 2 * T::K_BYTES + buf * T::V_BYTES, true); };
 
   // ---- per-lane constants of the transposed V read (ds_read_b64_tr_b16) ----
   // In each 16-lane group, source lane s points at row base + s/4, columns
@@ -168,8 +177,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_bf16_kernel(
   float m_ref = kNegInf, l_run = 0.f;
 
   // S^T = K Q^T for the block in K buffer `buf`: two 32-key sub-tiles.
-  auto qk = [&](int buf, f32x16 (&s)[2]) {
-    const unsigned char* kl = lds + buf * T::K_BYTES;
+  auto qk = [&](const unsigned char* kl, f32x16 (&s)[2]) {
     s[0] = f32x16{};
     s[1] = f32x16{};
 #pragma unroll
@@ -184,14 +192,14 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_bf16_kernel(
     }
   };
 
-  f32x16 s_cur[2], s_nxt[2];
+  f32x16 s_a[2], s_b[2];  // scores of the block being finished and of the next one; roles swap each block
 
-  // Softmax of block jb (scores in s_cur), QK of block jb+1 into s_nxt, then
-  // O^T += V^T P^T for block jb.
-  auto compute = [&](int jb, auto masked) {
+  // Block jb: softmax of its scores s, QK of block jb+1 (K in k_next) into
+  // s_next, then O^T += V^T P^T for block jb (V in vl).
+  auto compute = [&](int jb, const unsigned char* k_next, const unsigned char* vl, f32x16(&s)[2],
+                     f32x16(&s_next)[2], auto masked) {
     constexpr bool MASK = decltype(masked)::value;
     const int j0 = jb * BN;
-    f32x16(&s)[2] = s_cur;
 
     // ---- mask: keys past the end, keys after the query (causal) ----
     if (MASK) {
@@ -213,7 +221,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_bf16_kernel(
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+    mx = pair_max(mx) * c;
     // Move the reference only when the max outgrows it by more than 2^8.
     if (__ballot(mx > m_ref + kRescaleSlack)) {
       const float m_new = fmaxf(m_ref, mx);
@@ -228,10 +236,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_bf16_kernel(
     const float m_use = m_ref == kNegInf ? 0.f : m_ref;
 
     // ---- next block's scores (MFMA), overlapping the exponentials below (VALU).
-    // On the last block this reads the other K buffer's stale contents and the
-    // result is discarded; computing it unconditionally keeps the loop body
-    // branch-free. ----
-    qk((jb + 1) & 1, s_nxt);
+    // The masked body scores the next block after its PV instead (fewer live
+    // registers; it runs on a few blocks per tile only). ----
+    if (!MASK) qk(k_next, s_next);
 
     // P is rounded to bf16 once; the same rounded values feed the PV MFMA and
     // the denominator, so the weights of a row sum to exactly one.
@@ -247,7 +254,6 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_bf16_kernel(
       }
 
     // ---- O^T += V^T P^T: A operand = 8 keys of column d, two transposed reads ----
-    const unsigned char* vl = lds + 2 * T::K_BYTES + (jb & 1) * T::V_BYTES;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -269,38 +275,52 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_bf16_kernel(
 
   // ---- prologue: K0, V0, K1 in LDS; scores of block 0 ----
   // nblk >= 1: every query row sees at least key 0.
-  load_k(0, 0);
-  load_v(0, 0);
-  if (nblk > 1) load_k(BN, 1);
+  dma_block(kr, 0, lds_k0, false);
+  dma_block(vr, 0, lds_v0, true);
+  if (nblk > 1) dma_block(kr, BN, lds_k1, false);
   wait_vmem();
   __syncthreads();
-  qk(0, s_cur);
+  qk(lds_k0, s_a);
 
-  // Iteration jb: streams K[jb+2] into the K buffer block jb used and V[jb+1]
-  // into the V buffer block jb-1 used (both free since the last barrier),
-  // then runs block jb.
-  auto step = [&](int jb, auto masked) {
+  // Iteration jb streams K[jb+2] into the K buffer block jb used and V[jb+1]
+  // into the V buffer block jb-1 used (both free since the last barrier), then
+  // runs block jb.  Block jb's K and V sit in buffers jb % 2.
+  auto step = [&](int jb, unsigned char* k_cur, unsigned char* k_nxt, unsigned char* v_cur, unsigned char* v_nxt,
+                  f32x16(&s)[2], f32x16(&s_next)[2], auto masked) {
     const bool next1 = jb + 1 < nblk, next2 = jb + 2 < nblk;
-    if (next2) load_k((jb + 2) * BN, jb & 1);
-    if (next1) load_v((jb + 1) * BN, (jb + 1) & 1);
-    // A wavefront whose rows all precede this block sees none of it (its
-    // scores for the next block are still computed: they may be visible).
-    if (!decltype(masked)::value || !(cmask && jb * BN > wave_row_last)) {
-      compute(jb, masked);
-    } else {
-      qk((jb + 1) & 1, s_nxt);
-    }
-#pragma unroll
-    for (int t = 0; t < 2; ++t) s_cur[t] = s_nxt[t];
+    if (next2) dma_block(kr, (jb + 2) * BN, k_cur, false);
+    if (next1) dma_block(vr, (jb + 1) * BN, v_nxt, true);
+    // A wavefront whose rows all precede this block sees none of it.
+    if (!decltype(masked)::value || !(cmask && jb * BN > wave_row_last)) compute(jb, k_nxt, v_cur, s, s_next, masked);
+    if (decltype(masked)::value && next1) qk(k_nxt, s_next);
     wait_vmem();
     __syncthreads();
   };
+  // Blocks [0, n_free) run the mask-free body, two at a time so that every
+  // buffer and score set is fixed at compile time (the compiler then sees that
+  // the DMA of one buffer cannot alias reads of another).  The rest (diagonal
+  // blocks, a ragged tail, and always the last block, which has no next block
+  // to score) run the masked body with the buffers picked at run time.
+  const int n_free = n_full < nblk - 1 ? n_full : nblk - 1;
   int jb = 0;
-  for (; jb < n_full; ++jb) step(jb, std::false_type{});
-  for (; jb < nblk; ++jb) step(jb, std::true_type{});
+  for (; jb + 2 <= n_free; jb += 2) {
+    step(jb, lds_k0, lds_k1, lds_v0, lds_v1, s_a, s_b, std::false_type{});
+    step(jb + 1, lds_k1, lds_k0, lds_v1, lds_v0, s_b, s_a, std::false_type{});
+  }
+  if (jb < n_free) {
+    step(jb, lds_k0, lds_k1, lds_v0, lds_v1, s_a, s_b, std::false_type{});
+    ++jb;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) s_a[t] = s_b[t];
+  }
+  for (; jb < nblk; ++jb) {
+    const bool odd = jb & 1;
+    step(jb, odd ? lds_k1 : lds_k0, odd ? lds_k0 : lds_k1, odd ? lds_v1 : lds_v0, odd ? lds_v0 : lds_v1, s_a, s_a,
+         std::true_type{});
+  }
 
   // ---- epilogue: O = acc / l, bf16 round-to-nearest-even ----
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float l_tot = pair_sum(l_run);
   const float inv = 1.0f / l_tot;
   if (q < Sq) {
     uint16_t* op = Og + q_base + (size_t)q * D;

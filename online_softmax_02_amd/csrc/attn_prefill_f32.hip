@@ -264,8 +264,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_f32_kernel(
   }
 }
 
-// Merge the key slices of each query row: one wavefront per row, lane c owns
-// columns c and c + 64.
+// Merge the key slices of each query row: one wavefront per row.  Lane s
+// (< splits <= 64) loads slice s's (m, l); the wavefront max and the weights
+// 2^(m_s - m) are shared by shuffles; lane c owns output columns c and c + 64.
 __global__ __launch_bounds__(256) void combine_f32_kernel(const float* __restrict__ ws_ml,
                                                           const float* __restrict__ ws_acc, float* __restrict__ Og,
                                                           int64_t rows, int splits, int d) {
@@ -273,13 +274,15 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(const float* __restric
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
   const float* ml = ws_ml + row * splits * 2;
-  float M = kNegInf;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, ml[2 * s]);
-  float L = 0.f, a0 = 0.f, a1 = 0.f;
+  const float m_s = lane < splits ? ml[2 * lane] : kNegInf;
+  const float l_s = lane < splits ? ml[2 * lane + 1] : 0.f;
+  const float M = wave_max(m_s);
+  const float w_s = lane < splits ? exp2_fast(m_s - M) : 0.f;  // 0 for an empty slice
+  const float L = wave_sum(l_s * w_s);
   const float* pa = ws_acc + row * splits * d;
+  float a0 = 0.f, a1 = 0.f;
   for (int s = 0; s < splits; ++s) {
-    const float w = exp2_fast(ml[2 * s] - M);  // 0 for an empty slice
-    L += ml[2 * s + 1] * w;
+    const float w = __shfl(w_s, s, 64);
     if (lane < d) a0 += pa[(int64_t)s * d + lane] * w;
     if (lane + 64 < d) a1 += pa[(int64_t)s * d + lane + 64] * w;
   }

@@ -37,6 +37,20 @@ constexpr float kNegInf = -__builtin_huge_valf();
 // 2^x on the transcendental unit (v_exp_f32); exp2(-inf) = 0.
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Reductions over lane pairs (i, i ^ 32) with v_permlane32_swap, which trades
+// the upper 32 lanes of one register for the lower 32 of another in the VALU
+// (no LDS round trip).  Swapping two copies of v leaves, in every lane, one
+// register with v of lane i mod 32 and one with v of lane i mod 32 + 32, so
+// both halves compute the same expression in the same order.
+__device__ __forceinline__ float pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Butterfly reductions over all 64 lanes of a wavefront.
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
