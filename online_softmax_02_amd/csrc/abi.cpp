@@ -70,9 +70,11 @@ int plan_attn(int dtype, int batch, int heads_q, int heads_kv, int seq_q, int se
     return ok();
   }
   const int hp = heads_per_wg(groups);
-  const int rows_per_wg = osx::kRowsPerWave * (osx::kAttnWaves / hp);
+  // bf16: two groups of 4 wavefronts, the second on the rows after the first's.
+  const int rows_per_wg = dtype == OSX_BF16 ? osx::kRowsPerWave * (osx::kPrefillWaves / hp)
+                                            : osx::kRowsPerWave * (osx::kAttnWaves / hp);
   p->kernel = dtype == OSX_BF16 ? OSX_KERNEL_PREFILL_BF16 : OSX_KERNEL_PREFILL_F32;
-  p->threads = osx::kAttnThreads;
+  p->threads = dtype == OSX_BF16 ? osx::kPrefillThreads : osx::kAttnThreads;
   p->block_m = rows_per_wg;
   p->block_n = dtype == OSX_BF16 ? osx::kBf16BlockN : osx::kF32BlockN;
   p->splits = 1;

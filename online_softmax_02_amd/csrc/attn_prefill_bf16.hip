@@ -9,29 +9,40 @@
 // 2^(m_old - m_new) when the max grows.  At the end O = acc / l.
 //
 // How it maps onto CDNA4:
-//  * A workgroup is 4 wavefronts.  Each wavefront owns 32 query rows of one
-//    query head; the workgroup's wavefronts share one KV head (GQA: query head h
-//    reads KV head h / G), either 4 heads x 32 rows, 2 x 64 or 1 x 128.
-//  * K and V blocks of 64 keys are staged through LDS (two buffers each, one
-//    barrier per block) with 16-byte direct-to-LDS buffer loads (no register
-//    staging); rows past the end read as 0.
-//    K runs one block ahead: the QK MFMAs of block j+1 are issued while the
-//    exponentials of block j run on the VALU, then block j's PV MFMAs follow.
+//  * A workgroup is 8 wavefronts in two groups of 4, one workgroup per CU, so
+//    each SIMD runs one wavefront of each group.  Each wavefront owns 32 query
+//    rows of one query head; all 8 share one KV head (GQA: query head h reads
+//    KV head h / G).  The second group holds the 32-row tiles that follow the
+//    first group's.
+//  * The groups alternate between two phases, separated by workgroup barriers:
+//    an MFMA phase (scores of key block j+1, then O += P V for block j) and a
+//    softmax phase (max, exponentials, bf16 P and row sums for block j+1).
+//    Group B runs one phase behind group A, so on every SIMD one wavefront
+//    feeds the matrix cores while the other runs the exponentials.
+//  * K and V blocks of 64 keys are staged through LDS in 4 stages with 16-byte
+//    direct-to-LDS buffer loads (rows past the end read as 0); stage s holds K
+//    of block j+1 and V of block j for j = s mod 4.  A stage is loaded three
+//    blocks before its MFMA phase, by all 8 wavefronts, and each wavefront
+//    only waits for its loads of the stage two blocks ahead (loads past the
+//    last block are issued anyway, so every wait has a fixed count).  The loop is
+//    unrolled by 4 so every stage is a fixed LDS object: the compiler then
+//    knows that a read of one stage does not wait for a load into another.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //    a lane then holds 16 scores of ONE query, so the row max and row sum are
-//    lane-local (plus one cross-half exchange for the max per block) and the
-//    rescale factor is a per-lane scalar.
+//    lane-local (plus one permlane exchange between the two lane halves) and
+//    the rescale factor is a per-lane scalar.
 //  * The output is also accumulated transposed, O^T += V^T P^T, with P (rounded
-//    to bf16 once) taken straight from the score registers as the B operand.
-//    V stays row-major in LDS; ds_read_b64_tr_b16 delivers it transposed.
+//    to bf16 once) taken from the score registers as the B operand.  V stays
+//    row-major in LDS; ds_read_b64_tr_b16 delivers it transposed.
 //  * exp is 2^(s*c - m) with c = scale*log2(e) folded into one FMA; m lives in
 //    that log2 domain.  The reference m used in the exponent is moved (and acc,
 //    l rescaled by 2^(m_old - m_new)) only when a row's running max exceeds it
 //    by more than 2^8; the result is identical in exact arithmetic (the page's
 //    shift invariance) and the exponentials stay <= 2^8.
 //  * Causal: key blocks wholly after the workgroup's last query are never
-//    visited; blocks that need no mask (the prefix before the diagonal) run a
-//    mask-free copy of the loop body; tiles are dispatched heaviest first.
+//    visited, a wavefront skips the work of blocks that lie wholly after its
+//    own rows, and only blocks that cross the diagonal (or the end of the keys)
+//    are masked; tiles are dispatched heaviest first.
 #include <type_traits>
 
 #include "common.hpp"
@@ -40,7 +51,9 @@
 namespace osx {
 namespace {
 
-constexpr int BN = kBf16BlockN;  // 64 keys per block
+constexpr int BN = kBf16BlockN;        // 64 keys per block
+constexpr int kGroupWaves = kPrefillWaves / 2;
+constexpr int kStages = 4;
 constexpr float kRescaleSlack = 8.0f;  // log2 units a row max may exceed the reference before a rescale
 
 typedef __attribute__((ext_vector_type(4))) short i16x4;
@@ -49,13 +62,16 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 template <int D>
 struct Bf16Tile {
-  static constexpr int CH = D / 8;               // 16-byte chunks per K/V row
-  static constexpr int KC = D / 16;              // k-steps of the QK MFMA
-  static constexpr int DT = D / 32;              // 32-row d tiles of the PV MFMA
-  static constexpr int ROW = D * 2;              // bytes per K/V row in LDS
-  static constexpr int K_BYTES = BN * ROW;       // one K block in LDS
-  static constexpr int V_BYTES = BN * ROW;       // one V block in LDS
-  static constexpr int KU = BN * CH / kAttnThreads;  // 16-byte loads per thread, K (and V)
+  static constexpr int CH = D / 8;                       // 16-byte chunks per K/V row
+  static constexpr int KC = D / 16;                      // k-steps of the QK MFMA
+  static constexpr int DT = D / 32;                      // 32-row d tiles of the PV MFMA
+  static constexpr int ROW = D * 2;                      // bytes per K/V row in LDS
+  static constexpr int BLOCK_BYTES = BN * ROW;           // one K or V block in LDS
+  static constexpr int LDS_ROWS = 64 / CH;               // rows per 1 KiB direct-to-LDS instruction
+  static constexpr int DMA_INSTS = BN / LDS_ROWS;        // instructions per K (or V) block
+  static constexpr int DMA_PER_WAVE = DMA_INSTS / kPrefillWaves;
+  static_assert(DMA_INSTS % kPrefillWaves == 0, "each wavefront loads an equal share of a block");
+  static_assert((kPrefillWaves * LDS_ROWS) % 16 == 0, "a wavefront's rows keep their swizzle across instructions");
 };
 
 // K row chunk swizzle: the 16 rows one MFMA read touches land in 16 distinct
@@ -73,23 +89,45 @@ __device__ __forceinline__ int v_swz(int row) {
   return CH % 16 == 0 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
 }
 
+// s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+// Phase boundary: no instruction is scheduled across it, every LDS read of
+// the phase has returned, and all 8 wavefronts arrive before any goes on.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 template <int D>
-__global__ __launch_bounds__(kAttnThreads, 2) void prefill_bf16_kernel(
+__global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
     const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, const uint16_t* __restrict__ Vg,
     uint16_t* __restrict__ Og, int Hq, int Hkv, int Sq, int Sk, int causal, float c, int hp, int n_hgroups,
     int n_qtiles, int units_per_tile) {
   using T = Bf16Tile<D>;
-  // Four separate LDS objects (two K, two V buffers): the compiler can then
-  // tell a read of one buffer from a DMA into another and does not wait for
-  // the DMA before the read.
-  __shared__ __attribute__((aligned(16))) unsigned char lds_k0[T::K_BYTES];
-  __shared__ __attribute__((aligned(16))) unsigned char lds_k1[T::K_BYTES];
-  __shared__ __attribute__((aligned(16))) unsigned char lds_v0[T::V_BYTES];
-  __shared__ __attribute__((aligned(16))) unsigned char lds_v1[T::V_BYTES];
+  // One LDS object per stage and operand, so that every access names a fixed object.
+  __shared__ __attribute__((aligned(16))) unsigned char lds_k0[T::BLOCK_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_k1[T::BLOCK_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_k2[T::BLOCK_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_k3[T::BLOCK_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_v0[T::BLOCK_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_v1[T::BLOCK_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_v2[T::BLOCK_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_v3[T::BLOCK_BYTES];
+  // Stages are indexed with constants only (every call below passes a literal
+  // stage), so after inlining each access names one fixed LDS object.
+  unsigned char* const k_stage[kStages] = {lds_k0, lds_k1, lds_k2, lds_k3};
+  unsigned char* const v_stage[kStages] = {lds_v0, lds_v1, lds_v2, lds_v3};
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps per-wave values in SGPRs
+  const int grp = wave / kGroupWaves, wq = wave % kGroupWaves;
   const int l32 = lane & 31, hf = lane >> 5;
 
   // ---- work decomposition (consecutive workgroups share the q tile and walk
@@ -101,10 +139,11 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_bf16_kernel(
   const int b = rem / (Hkv * n_hgroups);
   const int kvh = (rem / n_hgroups) % Hkv;
   const int hg = rem % n_hgroups;
-  const int rs = kAttnWaves / hp;
-  const int head = kvh * G + hg * hp + (wave % hp);
-  const int wg_row0 = qt * kRowsPerWave * rs;
-  const int row0 = wg_row0 + (wave / hp) * kRowsPerWave;
+  const int rs = kGroupWaves / hp;  // 32-row tiles per group and head
+  const int head = kvh * G + hg * hp + (wq % hp);
+  const int wg_rows = 2 * kRowsPerWave * rs;
+  const int wg_row0 = qt * wg_rows;
+  const int row0 = wg_row0 + (grp * rs + wq / hp) * kRowsPerWave;
   const int q = row0 + l32;
 
   const size_t q_base = (size_t)(b * Hq + head) * Sq * D;
@@ -121,46 +160,59 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_bf16_kernel(
     qreg[kc] = __builtin_bit_cast(bf16x8, buf_ld16(qr, (uint32_t)(q * D + kc * 16 + hf * 8) * 2));
 
   // ---- key range ----
-  int wg_row_end = wg_row0 + kRowsPerWave * rs;
+  int wg_row_end = wg_row0 + wg_rows;
   if (wg_row_end > Sq) wg_row_end = Sq;
   const bool cmask = causal && Sq > 1;
   const int n_keys = cmask ? (wg_row_end < Sk ? wg_row_end : Sk) : Sk;
-  const int nblk = (n_keys + BN - 1) / BN;
-  // Blocks [0, n_full) need no mask for any row of the workgroup.
-  int n_full = Sk / BN;
-  if (cmask) {
-    const int diag = (wg_row0 + 1) / BN;  // blocks with j0 + BN - 1 <= wg_row0
-    n_full = n_full < diag ? n_full : diag;
-  }
-  if (n_full > nblk) n_full = nblk;
+  const int nblk = (n_keys + BN - 1) / BN;  // >= 1: the workgroup's first row exists and sees key 0
+  const bool wave_live = row0 < Sq;
   const int wave_row_last = row0 + kRowsPerWave - 1;
+  // Does this wavefront's work include block j?  (Blocks wholly after its rows do not.)
+  auto visible = [&](int j) { return wave_live && j < nblk && (!cmask || j * BN <= wave_row_last); };
+  // Does block j need the mask for some row of this wavefront?
+  auto needs_mask = [&](int j) { return j * BN + BN > Sk || (cmask && j * BN + BN - 1 > row0); };
 
   // ---- global -> LDS staging with buffer_load_dwordx4 ... lds ----
-  // LDS holds two K buffers and two V buffers.  K runs one block ahead of V:
-  // while block jb's softmax and PV run, the QK of block jb+1 is issued.
   // A direct-to-LDS load writes lane i's 16 bytes at M0 + 16 i, so each lane
-  // fetches the global chunk that belongs in its (swizzled) LDS slot.
-  // One wavefront instruction fills LDS_ROWS rows; the block needs LDS_STEPS
-  // such instructions, spread over the 4 wavefronts.
-  constexpr int LDS_ROWS = 64 / T::CH;                 // rows per 1 KiB instruction
-  constexpr int LDS_STEPS = BN / LDS_ROWS / kAttnWaves;  // instructions per wavefront per block
+  // fetches the global chunk that belongs in its (swizzled) LDS slot.  One
+  // instruction fills LDS_ROWS rows; instructions r * 8 + wave are this
+  // wavefront's.  The swizzle of a row depends only on its position within 16
+  // rows, which r does not change: the lane's byte offset is fixed and the
+  // block and instruction offsets go into the scalar soffset.
   const int dma_row = lane / T::CH, dma_chunk = lane % T::CH;
-  // The swizzle of a row depends only on its position within 16 rows, which
-  // the instruction index does not change: the lane's byte offset is fixed and
-  // the block and instruction offsets go into the scalar soffset.
-  const int dma_row0 = wave * LDS_ROWS + dma_row;
+  const int dma_row0 = wave * T::LDS_ROWS + dma_row;
   const int k_voff = (dma_row0 * D + ((dma_chunk ^ k_swz<T::CH>(dma_row0)) << 3)) * 2;
   const int v_voff = (dma_row0 * D + ((dma_chunk ^ v_swz<T::CH>(dma_row0)) << 3)) * 2;
-  static_assert((kAttnWaves * LDS_ROWS) % 16 == 0, "row swizzle must repeat every instruction step");
-  auto dma_block = [&](__amdgpu_buffer_rsrc_t rsrc, int j0, unsigned char* dst, bool is_v) {
+  auto dma_one = [&](__amdgpu_buffer_rsrc_t rsrc, int voff, int j0, unsigned char* dst, int r) {
+    const int inst = r * kPrefillWaves + wave;  // uniform
+    const int soff = (j0 + r * kPrefillWaves * T::LDS_ROWS) * D * 2;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(dst + inst * 1024), 16,
+                                             voff, soff, 0, 0);
+  };
+  auto dma_block = [&](__amdgpu_buffer_rsrc_t rsrc, int voff, int j0, unsigned char* dst) {
 #pragma unroll
-    for (int r = 0; r < LDS_STEPS; ++r) {
-      const int inst = r * kAttnWaves + wave;  // uniform
+    for (int r = 0; r < T::DMA_PER_WAVE; ++r) {
+      const int inst = r * kPrefillWaves + wave;  // uniform
+      // (soffset goes through a local: written inline as the builtin's
+      // argument, this expression kept the host compiler from emitting the
+      // kernel's launch stub.)
+      const int soff = (j0 + r * kPrefillWaves * T::LDS_ROWS) * D * 2;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(dst + inst * 1024),
-                                               16, is_v ? v_voff : k_voff,
-                                               (j0 + r * kAttnWaves * LDS_ROWS) * D * 2, 0, 0);
+                                               16, voff, soff, 0, 0);
     }
   };
+  // Stage of block j: K of block j+1 and V of block j.  Every stage is issued
+  // whole, also past the last block (those rows read as zeros or are never
+  // used), so each phase issues a fixed number of loads and every wait below
+  // has a fixed count; the compiler can then tell which loads have landed.
+  auto load_k = [&](int j0, unsigned char* dst) { dma_block(kr, k_voff, j0, dst); };
+  auto load_v = [&](int j0, unsigned char* dst) { dma_block(vr, v_voff, j0, dst); };
+  auto load_stage = [&](int stage, int j) {
+    load_k((j + 1) * BN, k_stage[stage % kStages]);
+    load_v(j * BN, v_stage[stage % kStages]);
+  };
+  constexpr int kStageLoads = 2 * T::DMA_PER_WAVE;  // per wavefront
+  static_assert(kStageLoads < 16, "vmcnt immediate");
 
   // ---- per-lane constants of the transposed V read (ds_read_b64_tr_b16) ----
   // In each 16-lane group, source lane s points at row base + s/4, columns
@@ -171,38 +223,102 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_bf16_kernel(
   const int v_col = 16 * (grp16 & 1) + 4 * (s16 & 3);  // + 32 dt
   const int v_row = 4 * (grp16 >> 1) + (s16 >> 2);     // + 32 t + 16 u (+ 8 for the upper 4 keys)
 
+  // Per-lane LDS byte offsets inside a stage buffer.  K fragment (kc, t) sits
+  // at k_off[kc] + 32 t rows; V fragment (t, u, dt) at v_off[dt] + (32 t + 16 u)
+  // rows (+ 8 rows for its upper half): the row terms keep the swizzle
+  // unchanged, so they are instruction immediates.
+  int k_off[T::KC], v_off[T::DT];
+#pragma unroll
+  for (int kc = 0; kc < T::KC; ++kc) k_off[kc] = l32 * T::ROW + (((2 * kc + hf) ^ k_swz<T::CH>(l32)) << 4);
+#pragma unroll
+  for (int dt = 0; dt < T::DT; ++dt) {
+    const int col = 32 * dt + v_col;
+    v_off[dt] = v_row * T::ROW + (((col >> 3) ^ v_swz<T::CH>(v_row)) << 4) + (col & 7) * 2;
+  }
+  auto k_addr = [&](const unsigned char* kl, int kc, int t) { return kl + k_off[kc] + 32 * t * T::ROW; };
+  auto v_addr = [&](const unsigned char* vl, int t, int u, int dt, int hi) {
+    return vl + v_off[dt] + (32 * t + 16 * u + 8 * hi) * T::ROW;
+  };
+
   f32x16 acc[T::DT];
 #pragma unroll
   for (int i = 0; i < T::DT; ++i) acc[i] = f32x16{};
-  float m_ref = kNegInf, l_run = 0.f;
+  float m_ref = kNegInf;
+  // Row sums of the bf16 weights, accumulated on the matrix cores: an A
+  // operand of ones turns each PV step into a row sum, so every element of
+  // this tile holds l for the lane's query (in fp32, exactly as the PV sees P).
+  f32x16 acc_l = f32x16{};
+  f32x16 s[2];      // scores of the block the next softmax phase handles
+  bf16x8 pb[2][2];  // its bf16 weights, the B operand of the next PV
 
-  // S^T = K Q^T for the block in K buffer `buf`: two 32-key sub-tiles.
-  auto qk = [&](const unsigned char* kl, f32x16 (&s)[2]) {
+  // S^T = K Q^T for one block: two 32-key sub-tiles.
+  auto qk = [&](const unsigned char* kl) {
     s[0] = f32x16{};
     s[1] = f32x16{};
 #pragma unroll
     for (int kc = 0; kc < T::KC; ++kc) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const int key = 32 * t + l32;
-        const int ch = 2 * kc + hf;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kl + key * T::ROW + ((ch ^ k_swz<T::CH>(key)) << 4));
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(k_addr(kl, kc, t));
         s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kc], s[t], 0, 0, 0);
       }
     }
   };
 
-  f32x16 s_a[2], s_b[2];  // scores of the block being finished and of the next one; roles swap each block
+  // MFMA phase: scores of the next block (K in kl), O^T += V^T P^T for this
+  // block (V in vl; the A operand is 8 keys of column d, from two transposed
+  // reads) and the loads of stage `jn` into k_dst / v_dst.  The order is fixed by
+  // hand (sched_barrier fences): the LDS read of each MFMA's fragment is
+  // issued kAhead MFMAs earlier, into a ring of registers, and the loads of
+  // the later stage are spread over the score MFMAs.
+  auto gemm_fast = [&](const unsigned char* kl, const unsigned char* vl, unsigned char* k_dst,
+                       unsigned char* v_dst, int jn) {
+    constexpr int NQ = 2 * T::KC, NP = 4 * T::DT, N = NQ + NP;
+    constexpr int kAhead = 6, kRing = 8;
+    auto frag = [&](int m) -> bf16x8 {
+      if (m < NQ) return *reinterpret_cast<const bf16x8*>(k_addr(kl, m >> 1, m & 1));
+      const int i = m - NQ;
+      const int t = i / (2 * T::DT), u = (i / T::DT) % 2, dt = i % T::DT;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v_addr(vl, t, u, dt, 0)));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v_addr(vl, t, u, dt, 1)));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    constexpr int kDmaEvery = NQ / (2 * T::DMA_PER_WAVE);
+    const bf16x8 kOnes = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+    bf16x8 ring[kRing];
+#pragma unroll
+    for (int m = 0; m < kAhead; ++m) ring[m % kRing] = frag(m);
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+#pragma unroll
+    for (int m = 0; m < N; ++m) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (m + kAhead < N) ring[(m + kAhead) % kRing] = frag(m + kAhead);
+      if (m < NQ) {
+        s[m & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[m % kRing], qreg[m >> 1], s[m & 1], 0, 0, 0);
+        if (m % kDmaEvery == kDmaEvery - 1) {  // one direct-to-LDS load of stage jn
+          const int d = m / kDmaEvery;           // 0 .. 2 * DMA_PER_WAVE - 1
+          const int r = d % T::DMA_PER_WAVE;
+          if (d < T::DMA_PER_WAVE) dma_one(kr, k_voff, (jn + 1) * BN, k_dst, r);
+          else dma_one(vr, v_voff, jn * BN, v_dst, r);
+        }
+      } else {
+        const int i = m - NQ;
+        acc[i % T::DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[m % kRing], pb[i / (2 * T::DT)][(i / T::DT) % 2],
+                                                                 acc[i % T::DT], 0, 0, 0);
+        if (i % T::DT == T::DT - 1)  // row sums of this (t, u) slice of P
+          acc_l = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kOnes, pb[i / (2 * T::DT)][(i / T::DT) % 2], acc_l, 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
-  // Block jb: softmax of its scores s, QK of block jb+1 (K in k_next) into
-  // s_next, then O^T += V^T P^T for block jb (V in vl).
-  auto compute = [&](int jb, const unsigned char* k_next, const unsigned char* vl, f32x16(&s)[2],
-                     f32x16(&s_next)[2], auto masked) {
-    constexpr bool MASK = decltype(masked)::value;
-    const int j0 = jb * BN;
-
-    // ---- mask: keys past the end, keys after the query (causal) ----
-    if (MASK) {
+  // Softmax of block j (scores in s): mask, running max and lazy rescale,
+  // exponentials and bf16 weights into pb (their row sums are taken with the
+  // PV on the matrix cores).
+  auto softmax = [&](int j) {
+    const int j0 = j * BN;
+    if (needs_mask(j)) {
       // key j0 + 4hf + o is visible iff o < lim, o = 32t + 8(r/4) + r%4
       int lim = cmask ? (q + 1 < Sk ? q + 1 : Sk) : Sk;
       lim -= j0 + 4 * hf;
@@ -214,8 +330,6 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_bf16_kernel(
           s[t][r] = o < lim ? s[t][r] : kNegInf;
         }
     }
-
-    // ---- online softmax (log2 domain) ----
     float mx = s[0][0];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -227,22 +341,16 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_bf16_kernel(
       const float m_new = fmaxf(m_ref, mx);
       if (m_new != kNegInf) {  // a row with no visible key yet keeps the empty state
         const float alpha = exp2_fast(m_ref - m_new);  // 0 on the first visible block
-        l_run *= alpha;
+        acc_l *= alpha;
 #pragma unroll
         for (int i = 0; i < T::DT; ++i) acc[i] *= alpha;
         m_ref = m_new;
       }
     }
     const float m_use = m_ref == kNegInf ? 0.f : m_ref;
-
-    // ---- next block's scores (MFMA), overlapping the exponentials below (VALU).
-    // The masked body scores the next block after its PV instead (fewer live
-    // registers; it runs on a few blocks per tile only). ----
-    if (!MASK) qk(k_next, s_next);
-
     // P is rounded to bf16 once; the same rounded values feed the PV MFMA and
-    // the denominator, so the weights of a row sum to exactly one.
-    bf16x8 pb[2][2];
+    // the denominator, so the weights of a row sum to one (up to fp32 rounding
+    // of the sum).
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -250,77 +358,70 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_bf16_kernel(
         float p[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) p[i] = exp2_fast(fmaf(s[t][8 * u + i], c, -m_use));
-        pb[t][u] = pack_bf16x8_sum(p, l_run);
+        pb[t][u] = pack_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
       }
+  };
 
-    // ---- O^T += V^T P^T: A operand = 8 keys of column d, two transposed reads ----
+  // Block j at stage P = j mod 4.  MFMA phase: scores of block j+1 (K in stage
+  // P) and O += P V for block j (V in stage P).  Softmax phase: load stage
+  // P+3 (block j+3), softmax of block j+1, then wait for this wavefront's
+  // older loads (stage P+2 and before) so that after the barrier they are
+  // visible to all.
+  auto block = [&](int P, int j) {
+    __builtin_amdgcn_s_setprio(2);  // the MFMA phase wins issue slots over the other group's softmax
+    // Always the full MFMA phase: a block this wavefront cannot see has zero
+    // weights (its PV adds nothing) and its scores go unused.
+    gemm_fast(k_stage[P], v_stage[P], k_stage[(P + 3) % kStages], v_stage[(P + 3) % kStages], j + 3);
+    phase_barrier();
+    __builtin_amdgcn_s_setprio(0);
+    if (visible(j + 1)) {
+      softmax(j + 1);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) pb[t][u] = bf16x8{};
+    }
+    wait_vmcnt<kStageLoads>();
+    phase_barrier();
+  };
+
+  // ---- prologue: K of block 0 into stage 3, stages 0..2; scores and softmax of block 0 ----
+  // Stage 1 is read in the third phase, before group B's first wait; so only
+  // stage 2 may still be in flight at the first barrier.
+  load_k(0, k_stage[3]);
+  load_stage(0, 0);
+  load_stage(1, 1);
+  load_stage(2, 2);
+  wait_vmcnt<kStageLoads>();
+  phase_barrier();
+  if (visible(0)) {
+    qk(k_stage[3]);
+    softmax(0);
+  } else {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-#pragma unroll
-        for (int dt = 0; dt < T::DT; ++dt) {
-          const int col = 32 * dt + v_col;
-          const int r0 = 32 * t + 16 * u + v_row, r1 = r0 + 8;
-          const unsigned char* p0 = vl + r0 * T::ROW + (((col >> 3) ^ v_swz<T::CH>(r0)) << 4) + (col & 7) * 2;
-          const unsigned char* p1 = vl + r1 * T::ROW + (((col >> 3) ^ v_swz<T::CH>(r1)) << 4) + (col & 7) * 2;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
-          const i16x8 v8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v8), pb[t][u], acc[dt], 0,
-                                                            0, 0);
-        }
-      }
-  };
+      for (int u = 0; u < 2; ++u) pb[t][u] = bf16x8{};
+  }
+  phase_barrier();
+  if (grp == 1) phase_barrier();  // group B runs one phase behind group A
 
-  // ---- prologue: K0, V0, K1 in LDS; scores of block 0 ----
-  // nblk >= 1: every query row sees at least key 0.
-  dma_block(kr, 0, lds_k0, false);
-  dma_block(vr, 0, lds_v0, true);
-  if (nblk > 1) dma_block(kr, BN, lds_k1, false);
-  wait_vmem();
-  __syncthreads();
-  qk(lds_k0, s_a);
-
-  // Iteration jb streams K[jb+2] into the K buffer block jb used and V[jb+1]
-  // into the V buffer block jb-1 used (both free since the last barrier), then
-  // runs block jb.  Block jb's K and V sit in buffers jb % 2.
-  auto step = [&](int jb, unsigned char* k_cur, unsigned char* k_nxt, unsigned char* v_cur, unsigned char* v_nxt,
-                  f32x16(&s)[2], f32x16(&s_next)[2], auto masked) {
-    const bool next1 = jb + 1 < nblk, next2 = jb + 2 < nblk;
-    if (next2) dma_block(kr, (jb + 2) * BN, k_cur, false);
-    if (next1) dma_block(vr, (jb + 1) * BN, v_nxt, true);
-    // A wavefront whose rows all precede this block sees none of it.
-    if (!decltype(masked)::value || !(cmask && jb * BN > wave_row_last)) compute(jb, k_nxt, v_cur, s, s_next, masked);
-    if (decltype(masked)::value && next1) qk(k_nxt, s_next);
-    wait_vmem();
-    __syncthreads();
-  };
-  // Blocks [0, n_free) run the mask-free body, two at a time so that every
-  // buffer and score set is fixed at compile time (the compiler then sees that
-  // the DMA of one buffer cannot alias reads of another).  The rest (diagonal
-  // blocks, a ragged tail, and always the last block, which has no next block
-  // to score) run the masked body with the buffers picked at run time.
-  const int n_free = n_full < nblk - 1 ? n_full : nblk - 1;
-  int jb = 0;
-  for (; jb + 2 <= n_free; jb += 2) {
-    step(jb, lds_k0, lds_k1, lds_v0, lds_v1, s_a, s_b, std::false_type{});
-    step(jb + 1, lds_k1, lds_k0, lds_v1, lds_v0, s_b, s_a, std::false_type{});
+  int j = 0;
+  for (; j + kStages <= nblk; j += kStages) {
+    block(0, j);
+    block(1, j + 1);
+    block(2, j + 2);
+    block(3, j + 3);
   }
-  if (jb < n_free) {
-    step(jb, lds_k0, lds_k1, lds_v0, lds_v1, s_a, s_b, std::false_type{});
-    ++jb;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) s_a[t] = s_b[t];
-  }
-  for (; jb < nblk; ++jb) {
-    const bool odd = jb & 1;
-    step(jb, odd ? lds_k1 : lds_k0, odd ? lds_k0 : lds_k1, odd ? lds_v1 : lds_v0, odd ? lds_v0 : lds_v1, s_a, s_a,
-         std::true_type{});
-  }
+  if (j < nblk) block(0, j);
+  if (j + 1 < nblk) block(1, j + 1);
+  if (j + 2 < nblk) block(2, j + 2);
+  if (grp == 0) phase_barrier();  // group A ends one phase ahead: keep the barrier counts equal
+  wait_vmcnt<0>();  // no load into LDS may land after the workgroup has ended
 
   // ---- epilogue: O = acc / l, bf16 round-to-nearest-even ----
-  const float l_tot = pair_sum(l_run);
+  const float l_tot = acc_l[0];
   const float inv = 1.0f / l_tot;
   if (q < Sq) {
     uint16_t* op = Og + q_base + (size_t)q * D;
@@ -344,7 +445,7 @@ hipError_t launch(const AttnArgs& a) {
   const int rows_per_wg = a.plan.block_m;
   const int n_qtiles = (a.seq_q + rows_per_wg - 1) / rows_per_wg;
   const int units_per_tile = a.batch * a.heads_kv * n_hgroups;
-  hipLaunchKernelGGL(prefill_bf16_kernel<D>, dim3((unsigned)a.plan.grid), dim3(kAttnThreads), 0, a.stream,
+  hipLaunchKernelGGL(prefill_bf16_kernel<D>, dim3((unsigned)a.plan.grid), dim3(kPrefillThreads), 0, a.stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.heads_q, a.heads_kv, a.seq_q,
                      a.seq_k, a.causal, a.c, hp, n_hgroups, n_qtiles, units_per_tile);

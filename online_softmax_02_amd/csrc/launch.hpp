@@ -14,6 +14,8 @@ constexpr int kWaveSize = 64;
 constexpr int kAttnThreads = 256;     // 4 wavefronts per workgroup
 constexpr int kAttnWaves = 4;
 constexpr int kRowsPerWave = 32;      // query rows per wavefront (one 32-wide MFMA column tile)
+constexpr int kPrefillThreads = 512;  // bf16 prefill: 8 wavefronts in two alternating groups of 4
+constexpr int kPrefillWaves = 8;
 constexpr int kBf16BlockN = 64;       // keys per LDS block, bf16 prefill
 constexpr int kF32BlockN = 32;        // keys per LDS block, fp32 prefill
 constexpr int kDecodeBlockN = 32;     // keys per wavefront step, decode

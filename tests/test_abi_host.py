@@ -92,7 +92,7 @@ def test_no_work_is_ok_without_pointers():
 def test_plans_for_the_workloads():
     p = osx.attn_plan(BF16, 2, 32, 8, 4096, 4096, 128, True)
     assert p["kernel_name"] == "prefill_bf16" and p["heads_per_wg"] == 4 and p["workspace_bytes"] == 0
-    assert p["grid"] == 2 * 8 * (4096 // 32)
+    assert p["grid"] == 2 * 8 * (4096 // 64) and p["block_m"] == 64 and p["threads"] == 512
     p = osx.attn_plan(BF16, 64, 32, 8, 1, 8192, 128)
     assert p["kernel_name"] == "decode_bf16"
     assert p["workspace_bytes"] == osx.attn_fwd_workspace(BF16, 64, 32, 8, 1, 8192, 128)
