@@ -288,6 +288,13 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
     bf16x8 ring[kRing];
 #pragma unroll
     for (int m = 0; m < kAhead; ++m) ring[m % kRing] = frag(m);
+    // Row sums of this block's P first: they need no LDS data, so they cover
+    // the latency of the first reads.
+#pragma unroll
+    for (int tu = 0; tu < 4; ++tu) {
+      __builtin_amdgcn_sched_barrier(0);
+      acc_l = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kOnes, pb[tu >> 1][tu & 1], acc_l, 0, 0, 0);
+    }
     s[0] = f32x16{};
     s[1] = f32x16{};
 #pragma unroll
@@ -306,8 +313,6 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
         const int i = m - NQ;
         acc[i % T::DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[m % kRing], pb[i / (2 * T::DT)][(i / T::DT) % 2],
                                                                  acc[i % T::DT], 0, 0, 0);
-        if (i % T::DT == T::DT - 1)  // row sums of this (t, u) slice of P
-          acc_l = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kOnes, pb[i / (2 * T::DT)][(i / T::DT) % 2], acc_l, 0, 0, 0);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
