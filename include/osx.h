@@ -103,6 +103,24 @@ int osx_attn_fwd(const void* q, const void* k, const void* v, void* o, int dtype
                  int heads_kv, int seq_q, int seq_k, int head_dim, int causal, float scale, void* workspace,
                  size_t workspace_bytes, void* stream);
 
+/*
+ * osx_attn_fwd_lse -- osx_attn_fwd that also writes, for every query row, the
+ * natural log of its softmax denominator:
+ *     lse[(b * heads_q + h) * seq_q + i] = log sum_j exp(scale * q_i . k_j)
+ * over the keys visible to row i.  This is the final state of the online
+ * recurrence (page "Softmax 算子的实现与优化", section Online Softmax: the
+ * running max m and l = sum_j e^{x_j - m} after the last block) folded into
+ * one number, lse = m + log l; with it O (or the weights) of two key ranges
+ * can be merged later.
+ *
+ * lse: device pointer to batch * heads_q * seq_q fp32 values, written in full
+ * (NULL -> OSX_EINVAL); it must not overlap q, k, v, o or the workspace.
+ * Everything else as osx_attn_fwd.
+ */
+int osx_attn_fwd_lse(const void* q, const void* k, const void* v, void* o, float* lse, int dtype, int batch,
+                     int heads_q, int heads_kv, int seq_q, int seq_k, int head_dim, int causal, float scale,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
 /* osx_softmax_rows_plan -- kernel choice for x[rows, cols]; no HIP calls. */
 int osx_softmax_rows_plan(int64_t rows, int64_t cols, osx_plan* out);
 

@@ -55,6 +55,7 @@ def _load() -> ctypes.CDLL:
     lib.osx_attn_plan.argtypes = attn_shape + [ctypes.POINTER(Plan)]
     lib.osx_attn_fwd_workspace.argtypes = attn_shape + [ctypes.POINTER(_sz)]
     lib.osx_attn_fwd.argtypes = [_vp, _vp, _vp, _vp] + attn_shape + [_f, _vp, _sz, _vp]
+    lib.osx_attn_fwd_lse.argtypes = [_vp, _vp, _vp, _vp, _vp] + attn_shape + [_f, _vp, _sz, _vp]
     lib.osx_softmax_rows_plan.argtypes = [_i64, _i64, ctypes.POINTER(Plan)]
     lib.osx_softmax_rows_workspace.argtypes = [_i64, _i64, ctypes.POINTER(_sz)]
     lib.osx_softmax_rows.argtypes = [_vp, _vp, _i64, _i64, _vp, _sz, _vp]
@@ -63,7 +64,7 @@ def _load() -> ctypes.CDLL:
     lib.osx_last_error.argtypes = []
     lib.osx_last_error.restype = ctypes.c_char_p
     lib.osx_version.argtypes = []
-    for name in ("osx_attn_plan", "osx_attn_fwd_workspace", "osx_attn_fwd", "osx_softmax_rows_plan",
+    for name in ("osx_attn_plan", "osx_attn_fwd_workspace", "osx_attn_fwd", "osx_attn_fwd_lse", "osx_softmax_rows_plan",
                  "osx_softmax_rows_workspace", "osx_softmax_rows", "osx_version"):
         getattr(lib, name).restype = _i
     return lib
@@ -138,12 +139,15 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}: float32 or bfloat16")
 
 
-def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, workspace=None, stream=None):
+def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, workspace=None, stream=None,
+             return_lse: bool = False, lse=None):
     """O = softmax(mask(q k^T * scale)) v on the GPU.
 
     q: [B, Hq, Sq, D] (or [M, D] for one head), k, v: [B, Hkv, Sk, D] (or
     [N, D]); contiguous CUDA tensors of one dtype (float32 or bfloat16).
-    Query head h reads KV head h // (Hq // Hkv).  Returns a tensor like q.
+    Query head h reads KV head h // (Hq // Hkv).  Returns a tensor like q; with
+    ``return_lse`` also the float32 [B, Hq, Sq] (or [M]) log-sum-exp of each
+    row's scaled, masked scores (``lse`` may supply that tensor).
     """
     torch = _torch()
     squeeze = q.dim() == 2
@@ -172,9 +176,20 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(lib.osx_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), code, B, Hq, Hkv, Sq, Sk, D,
-                            int(causal), float(scale) if scale else 0.0, ws_ptr, ws_len, _stream(q, stream)))
-    return out[0, 0] if squeeze else out
+    sc = float(scale) if scale else 0.0
+    if not (return_lse or lse is not None):
+        _check(lib.osx_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), code, B, Hq, Hkv, Sq, Sk, D,
+                                int(causal), sc, ws_ptr, ws_len, _stream(q, stream)))
+        return out[0, 0] if squeeze else out
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    elif lse.numel() != B * Hq * Sq or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor of B * Hq * Sq elements")
+    _check(lib.osx_attn_fwd_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), code, B, Hq,
+                                Hkv, Sq, Sk, D, int(causal), sc, ws_ptr, ws_len, _stream(q, stream)))
+    if squeeze:
+        return out[0, 0], lse.reshape(-1)
+    return out, lse
 
 
 def softmax_rows(x, out=None, workspace=None, stream=None):

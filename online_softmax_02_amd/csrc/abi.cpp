@@ -149,14 +149,19 @@ int osx_attn_fwd_workspace(int dtype, int batch, int heads_q, int heads_kv, int 
   return st;
 }
 
-int osx_attn_fwd(const void* q, const void* k, const void* v, void* o, int dtype, int batch, int heads_q,
-                 int heads_kv, int seq_q, int seq_k, int head_dim, int causal, float scale, void* workspace,
-                 size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, bool want_lse, int dtype, int batch,
+             int heads_q, int heads_kv, int seq_q, int seq_k, int head_dim, int causal, float scale, void* workspace,
+             size_t workspace_bytes, void* stream) {
   osx_plan p;
   int st = plan_attn(dtype, batch, heads_q, heads_kv, seq_q, seq_k, head_dim, causal, &p);
   if (st != OSX_OK) return st;
   if (p.kernel == OSX_KERNEL_NONE) return ok();
   if (!q || !k || !v || !o) return fail(OSX_EINVAL, "null q, k, v or o pointer");
+  if (want_lse && !lse) return fail(OSX_EINVAL, "null lse pointer");
   if (p.workspace_bytes > 0 && (!workspace || workspace_bytes < p.workspace_bytes))
     return fail(OSX_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : (size_t)0,
                 p.workspace_bytes);
@@ -167,6 +172,12 @@ int osx_attn_fwd(const void* q, const void* k, const void* v, void* o, int dtype
   if (overlap(o, nq, q, nq) || overlap(o, nq, k, nkv) || overlap(o, nq, v, nkv) ||
       (p.workspace_bytes && overlap(o, nq, workspace, p.workspace_bytes)))
     return fail(OSX_EINVAL, "output overlaps an input or the workspace");
+  if (lse) {
+    const size_t nl = (size_t)batch * heads_q * seq_q * sizeof(float);
+    if (overlap(lse, nl, q, nq) || overlap(lse, nl, k, nkv) || overlap(lse, nl, v, nkv) || overlap(lse, nl, o, nq) ||
+        (p.workspace_bytes && overlap(lse, nl, workspace, p.workspace_bytes)))
+      return fail(OSX_EINVAL, "lse overlaps an input, the output or the workspace");
+  }
   osx::AttnArgs a;
   a.q = q;
   a.k = k;
@@ -181,6 +192,7 @@ int osx_attn_fwd(const void* q, const void* k, const void* v, void* o, int dtype
   a.causal = causal ? 1 : 0;
   a.c = (float)((double)scale * 1.4426950408889634);
   a.workspace = workspace;
+  a.lse = lse;
   a.stream = (hipStream_t)stream;
   a.plan = p;
   hipError_t e;
@@ -193,6 +205,24 @@ int osx_attn_fwd(const void* q, const void* k, const void* v, void* o, int dtype
   if (e == hipSuccess) e = hipGetLastError();
   if (e != hipSuccess) return fail(OSX_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int osx_attn_fwd(const void* q, const void* k, const void* v, void* o, int dtype, int batch, int heads_q,
+                 int heads_kv, int seq_q, int seq_k, int head_dim, int causal, float scale, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  return attn_fwd(q, k, v, o, nullptr, false, dtype, batch, heads_q, heads_kv, seq_q, seq_k, head_dim, causal, scale,
+                  workspace, workspace_bytes, stream);
+}
+
+int osx_attn_fwd_lse(const void* q, const void* k, const void* v, void* o, float* lse, int dtype, int batch,
+                     int heads_q, int heads_kv, int seq_q, int seq_k, int head_dim, int causal, float scale,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_fwd(q, k, v, o, lse, true, dtype, batch, heads_q, heads_kv, seq_q, seq_k, head_dim, causal, scale,
+                  workspace, workspace_bytes, stream);
 }
 
 int osx_softmax_rows_plan(int64_t rows, int64_t cols, osx_plan* out) {

@@ -239,7 +239,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void decode_bf16_kernel(
 // Merge the splits of one (batch, query head): O = sum acc_s 2^(m_s-m) / sum l_s 2^(m_s-m).
 template <int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restrict__ ws, uint16_t* __restrict__ Og,
-                                                           int Hq, int Hkv, int splits, int n_wg) {
+                                                           float* __restrict__ Lse, int Hq, int Hkv, int splits,
+                                                           int n_wg) {
   const int bh = blockIdx.x;
   const int b = bh / Hq, hq = bh % Hq;
   const int G = Hq / Hkv;
@@ -259,6 +260,8 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restri
     a += ws_acc[p * D + dd] * f;
   }
   const float o = a / l;
+  // log sum_j exp(scale * s_j) = ln 2 * (M + log2 l), M in the log2 domain
+  if (Lse && dd == 0) Lse[bh] = (M + log2f(l)) * kLn2;
   const uint32_t w = pack_bf16x2(o, 0.f);
   Og[(size_t)bh * D + dd] = (uint16_t)(w & 0xffffu);
 }
@@ -275,7 +278,7 @@ hipError_t launch(const AttnArgs& a) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel<D>, dim3((unsigned)(a.batch * a.heads_q)), dim3(D), 0, a.stream, ws,
-                     static_cast<uint16_t*>(a.o), a.heads_q, a.heads_kv, splits, (int)a.plan.grid);
+                     static_cast<uint16_t*>(a.o), a.lse, a.heads_q, a.heads_kv, splits, (int)a.plan.grid);
   return hipGetLastError();
 }
 

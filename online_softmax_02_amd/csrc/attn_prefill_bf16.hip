@@ -107,8 +107,8 @@ __device__ __forceinline__ void phase_barrier() {
 template <int D>
 __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
     const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, const uint16_t* __restrict__ Vg,
-    uint16_t* __restrict__ Og, int Hq, int Hkv, int Sq, int Sk, int causal, float c, int hp, int n_hgroups,
-    int n_qtiles, int units_per_tile) {
+    uint16_t* __restrict__ Og, float* __restrict__ Lse, int Hq, int Hkv, int Sq, int Sk, int causal, float c, int hp,
+    int n_hgroups, int n_qtiles, int units_per_tile) {
   using T = Bf16Tile<D>;
   // One LDS object per stage and operand, so that every access names a fixed object.
   __shared__ __attribute__((aligned(16))) unsigned char lds_k0[T::BLOCK_BYTES];
@@ -428,6 +428,9 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
   // ---- epilogue: O = acc / l, bf16 round-to-nearest-even ----
   const float l_tot = acc_l[0];
   const float inv = 1.0f / l_tot;
+  // log sum_j exp(scale * s_j) = ln 2 * (m + log2 l): the sum of 2^(s c) is 2^m l
+  // for whatever reference m the row ended with.
+  if (Lse && hf == 0 && q < Sq) Lse[(size_t)(b * Hq + head) * Sq + q] = (m_ref + log2f(l_tot)) * kLn2;
   if (q < Sq) {
     uint16_t* op = Og + q_base + (size_t)q * D;
 #pragma unroll
@@ -452,8 +455,8 @@ hipError_t launch(const AttnArgs& a) {
   const int units_per_tile = a.batch * a.heads_kv * n_hgroups;
   hipLaunchKernelGGL(prefill_bf16_kernel<D>, dim3((unsigned)a.plan.grid), dim3(kPrefillThreads), 0, a.stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                     static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.heads_q, a.heads_kv, a.seq_q,
-                     a.seq_k, a.causal, a.c, hp, n_hgroups, n_qtiles, units_per_tile);
+                     static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse, a.heads_q, a.heads_kv,
+                     a.seq_q, a.seq_k, a.causal, a.c, hp, n_hgroups, n_qtiles, units_per_tile);
   return hipGetLastError();
 }
 

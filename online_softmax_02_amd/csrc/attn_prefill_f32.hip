@@ -48,8 +48,9 @@ __device__ __forceinline__ int k_swz(int row) {
 template <int DP>
 __global__ __launch_bounds__(kAttnThreads, 2) void prefill_f32_kernel(
     const float* __restrict__ Qg, const float* __restrict__ Kg, const float* __restrict__ Vg, float* __restrict__ Og,
-    int Hq, int Hkv, int Sq, int Sk, int d, int causal, float c, int hp, int n_hgroups, int n_qtiles,
-    int units_per_tile, int splits, int keys_per_split, float* __restrict__ ws_ml, float* __restrict__ ws_acc) {
+    float* __restrict__ Lse, int Hq, int Hkv, int Sq, int Sk, int d, int causal, float c, int hp, int n_hgroups,
+    int n_qtiles, int units_per_tile, int splits, int keys_per_split, float* __restrict__ ws_ml,
+    float* __restrict__ ws_acc) {
   using T = F32Tile<DP>;
   __shared__ __attribute__((aligned(16))) unsigned char lds[2 * T::BUF];
 
@@ -231,6 +232,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_f32_kernel(
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (q < Sq) {
     if (splits == 1) {
+      // log sum_j exp(scale * s_j) = ln 2 * (m + log2 l), m in the log2 domain
+      if (Lse && hf == 0) Lse[row_id] = (m_run + log2f(l_tot)) * kLn2;
       const float inv = 1.0f / l_tot;
       float* op = Og + q_base + (size_t)q * d;
 #pragma unroll
@@ -269,7 +272,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_f32_kernel(
 // 2^(m_s - m) are shared by shuffles; lane c owns output columns c and c + 64.
 __global__ __launch_bounds__(256) void combine_f32_kernel(const float* __restrict__ ws_ml,
                                                           const float* __restrict__ ws_acc, float* __restrict__ Og,
-                                                          int64_t rows, int splits, int d) {
+                                                          float* __restrict__ Lse, int64_t rows, int splits, int d) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
@@ -287,6 +290,7 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(const float* __restric
     if (lane + 64 < d) a1 += pa[(int64_t)s * d + lane + 64] * w;
   }
   const float inv = 1.0f / L;
+  if (Lse && lane == 0) Lse[row] = (M + log2f(L)) * kLn2;
   if (lane < d) Og[row * d + lane] = a0 * inv;
   if (lane + 64 < d) Og[row * d + lane + 64] = a1 * inv;
 }
@@ -306,12 +310,12 @@ hipError_t launch(const AttnArgs& a) {
   float* ws_acc = splits == 1 ? nullptr : ws_ml + rows * splits * 2;
   hipLaunchKernelGGL(prefill_f32_kernel<DP>, dim3((unsigned)a.plan.grid), dim3(kAttnThreads), 0, a.stream,
                      static_cast<const float*>(a.q), static_cast<const float*>(a.k), static_cast<const float*>(a.v),
-                     static_cast<float*>(a.o), a.heads_q, a.heads_kv, a.seq_q, a.seq_k, a.head_dim, a.causal, a.c, hp,
-                     n_hgroups, n_qtiles, units_per_tile, splits, kps, ws_ml, ws_acc);
+                     static_cast<float*>(a.o), a.lse, a.heads_q, a.heads_kv, a.seq_q, a.seq_k, a.head_dim, a.causal,
+                     a.c, hp, n_hgroups, n_qtiles, units_per_tile, splits, kps, ws_ml, ws_acc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   hipLaunchKernelGGL(combine_f32_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, a.stream, ws_ml, ws_acc,
-                     static_cast<float*>(a.o), rows, splits, a.head_dim);
+                     static_cast<float*>(a.o), a.lse, rows, splits, a.head_dim);
   return hipGetLastError();
 }
 

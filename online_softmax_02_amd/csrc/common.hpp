@@ -32,6 +32,7 @@ __device__ __forceinline__ f32x4 buf_ld16f(__amdgpu_buffer_rsrc_t r, uint32_t by
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
 // 2^x on the transcendental unit (v_exp_f32); exp2(-inf) = 0.

@@ -35,6 +35,7 @@ struct AttnArgs {
   int batch, heads_q, heads_kv, seq_q, seq_k, head_dim, causal;
   float c;  // scale * log2(e): scores are exponentiated as 2^(s*c - m)
   void* workspace;
+  float* lse;  // optional: natural-log sum of exp(scaled, masked scores) per query row, or null
   hipStream_t stream;
   osx_plan plan;
 };

@@ -11,6 +11,9 @@ attention        the plain definition O = softmax(mask(Q K^T * scale)) V with
                  (page "从零开始写Qwen3（五-其一）使用Triton实现自注意力",
                  section 自注意力原理; page "softmax_attention", section 实现思路).
 attention_rows   the same definition for a chosen set of query rows of one head.
+attention_lse    log sum_j exp(score) per query row: the final (max, sum) state of
+                 the online recurrence as one number (page "Softmax 算子的实现与优化",
+                 section Online Softmax).
 softmax_rows     the stable row softmax (page "Softmax 算子的实现与优化", the
                  max-shifted definition; page "Puzzle 8: Long Softmax", its spec).
 recurrence       a blockwise model of the online recurrence (running max, running
@@ -22,8 +25,8 @@ Every function is pinned by ``tests/test_oracle_pins.py`` to values, closed
 forms and invariants the pages and the mathematics fix.  No function here is
 "parity unpinned".
 """
-from .attention import attention, attention_rows, bf16_bits_to_f64
+from .attention import attention, attention_lse, attention_rows, bf16_bits_to_f64
 from .softmax import softmax_rows
 from . import recurrence, brute
 
-__all__ = ["attention", "attention_rows", "softmax_rows", "bf16_bits_to_f64", "recurrence", "brute"]
+__all__ = ["attention", "attention_lse", "attention_rows", "softmax_rows", "bf16_bits_to_f64", "recurrence", "brute"]

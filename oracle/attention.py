@@ -81,3 +81,31 @@ def attention_rows(q_rows, k, v, rows, *, causal: bool = False, seq_q: int | Non
         i = np.asarray(rows)[:, None]
         s = np.where(j <= i, s, -np.inf)
     return _softmax_last(s) @ v
+
+
+def attention_lse(q, k, v=None, *, causal: bool = False, scale: float | None = None) -> np.ndarray:
+    """Log-sum-exp of each query row's scaled, masked scores, in fp64: [B, Hq, Sq].
+
+    LSE[b, h, i] = log sum_j exp(S[i, j]) over the visible keys j, with S the
+    same scaled (and causally masked) score matrix as in ``attention``.  It is
+    the final online state of page "Softmax 算子的实现与优化", section Online
+    Softmax, folded into one number: m + log l with m the row max and
+    l = sum_j e^{S[i, j] - m}.  (``v`` is accepted for symmetry and unused.)
+    """
+    q, k = _as_f64(q), _as_f64(k)
+    B, Hq, Sq, D = q.shape
+    Bk, Hkv, Sk, Dk = k.shape
+    assert Bk == B and Dk == D and Hq % Hkv == 0
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    keep = np.tril(np.ones((Sq, Sk), dtype=bool)) if causal and Sq > 1 else None
+    out = np.empty((B, Hq, Sq), dtype=np.float64)
+    for b in range(B):
+        for h in range(Hq):
+            s = (q[b, h] @ k[b, h // G].T) * scale
+            if keep is not None:
+                s = np.where(keep, s, -np.inf)
+            m = np.max(s, axis=-1)
+            out[b, h] = m + np.log(np.sum(np.exp(s - m[:, None]), axis=-1))
+    return out

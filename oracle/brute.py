@@ -47,3 +47,31 @@ def softmax(row):
     w = [math.exp(float(x) - mx) for x in row]
     tot = math.fsum(w)
     return [t / tot for t in w]
+
+
+def attention_lse(q, k, causal=False, scale=None):
+    """log sum_j exp(scaled score) per query row, nested lists [B][Hq][Sq]."""
+    B, Hq, Sq, D = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
+    Hkv, Sk = len(k[0]), len(k[0][0])
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out = []
+    for b in range(B):
+        ob = []
+        for h in range(Hq):
+            oh = []
+            for i in range(Sq):
+                sc = []
+                for j in range(Sk):
+                    if causal and Sq > 1 and j > i:
+                        continue
+                    t = 0.0
+                    for c in range(D):
+                        t += float(q[b][h][i][c]) * float(k[b][h // G][j][c])
+                    sc.append(t * scale)
+                mx = max(sc)
+                oh.append(mx + math.log(math.fsum(math.exp(x - mx) for x in sc)))
+            ob.append(oh)
+        out.append(ob)
+    return out

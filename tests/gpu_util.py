@@ -6,6 +6,11 @@ import oracle
 # Parity bars: fp32 max abs error 1e-5; bf16 |err| <= 2e-2 + 1e-2 |ref| per element.
 F32_ATOL = 1e-5
 BF16_ATOL, BF16_RTOL = 2e-2, 1e-2
+# Log-sum-exp of the scores.  fp32: the row max and the fp32 sum of up to a few
+# thousand terms, each scaled score accurate to ~1e-6 -> 5e-5 absolute.  bf16:
+# the sum is taken over P rounded to bf16 (relative error <= 2^-9 each, so the
+# sum's relative error is below 2^-9 and ln of it below 2e-3) -> 4e-3 absolute.
+LSE_F32_ATOL, LSE_BF16_ATOL = 5e-5, 4e-3
 
 
 def to_dev(a: np.ndarray, device="cuda"):

@@ -116,3 +116,16 @@ def test_gqa_heads_per_workgroup():
     assert osx.attn_plan(BF16, 1, 16, 8, 256, 256, 128)["heads_per_wg"] == 2
     assert osx.attn_plan(BF16, 1, 24, 2, 256, 256, 128)["heads_per_wg"] == 4
     assert osx.attn_plan(BF16, 1, 3, 1, 256, 256, 64)["heads_per_wg"] == 1
+
+
+def test_attn_fwd_lse_rejects_before_launch():
+    lib = osx.lib
+    a, b, c, o = (ctypes.c_void_p(x) for x in (0x100000, 0x200000, 0x300000, 0x400000))
+    st = lib.osx_attn_fwd_lse(a, b, c, o, None, F32, 1, 1, 1, 16, 16, 64, 0, 0.0, None, 0, None)
+    assert st == osx.OSX_EINVAL and "lse" in osx.last_error()
+    # lse overlapping the output
+    st = lib.osx_attn_fwd_lse(a, b, c, o, ctypes.c_void_p(0x400000 + 64), F32, 1, 1, 1, 16, 16, 64, 0, 0.0, None, 0,
+                              None)
+    assert st == osx.OSX_EINVAL and "overlap" in osx.last_error()
+    # no work: OK without pointers
+    assert lib.osx_attn_fwd_lse(None, None, None, None, None, BF16, 0, 4, 1, 16, 16, 128, 1, 0.0, None, 0, None) == 0

@@ -236,3 +236,67 @@ def test_bf16_bits_decoding():
     bits = np.array([0x3F80, 0xBF80, 0x4049, 0x0000, 0x7F7F], dtype=np.uint16)
     np.testing.assert_array_equal(oracle.bf16_bits_to_f64(bits),
                                   [1.0, -1.0, 3.140625, 0.0, 3.3895313892515355e38])
+
+
+# ---------------------------------------------------------------- log-sum-exp of the scores
+def test_lse_closed_form_counts_visible_keys():
+    """K = 0 makes every score 0: LSE is log(number of visible keys), log(i + 1) under the causal mask."""
+    B, Hq, Hkv, S, D = 1, 2, 1, 9, 4
+    q = RNG.standard_normal((B, Hq, S, D))
+    k = np.zeros((B, Hkv, S, D))
+    np.testing.assert_allclose(oracle.attention_lse(q, k), np.full((B, Hq, S), math.log(S)), rtol=1e-15)
+    want = np.log(np.arange(1, S + 1, dtype=np.float64))
+    np.testing.assert_allclose(oracle.attention_lse(q, k, causal=True)[0, 1], want, atol=1e-15)
+
+
+def test_lse_two_keys_is_logaddexp():
+    """d=4, q=(2,0,0,0), k0=(1,0,0,0), k1=0: scores 1 and 0, LSE = log(e + 1); the scale argument applies."""
+    q = np.array([[[[2.0, 0, 0, 0]]]])
+    k = np.array([[[[1.0, 0, 0, 0], [0, 0, 0, 0]]]])
+    assert abs(oracle.attention_lse(q, k)[0, 0, 0] - math.log(math.e + 1.0)) < 1e-15
+    assert abs(oracle.attention_lse(q, k, scale=0.25)[0, 0, 0] - math.log(math.exp(0.5) + 1.0)) < 1e-15
+    # huge scores stay finite: max shift applied
+    big = np.array([[[[2000.0, 0, 0, 0]]]])
+    assert abs(oracle.attention_lse(big, k)[0, 0, 0] - (1000.0 + math.log1p(math.exp(-1000.0)))) < 1e-12
+
+
+def test_lse_shifts_with_a_common_key_offset():
+    """Adding u to every key adds scale * q_i . u to every score of row i, hence to its LSE."""
+    q = RNG.standard_normal((1, 2, 6, 8))
+    k = RNG.standard_normal((1, 1, 11, 8))
+    u = RNG.standard_normal(8)
+    base = oracle.attention_lse(q, k)
+    shifted = oracle.attention_lse(q, k + u)
+    np.testing.assert_allclose(shifted, base + (q @ u) / math.sqrt(8), rtol=1e-12, atol=1e-12)
+
+
+def test_lse_matches_library_logsumexp_and_normalises_the_weights():
+    """scipy's logsumexp of the masked scores; exp(S - LSE) are the attention weights (they sum to 1)."""
+    q = RNG.standard_normal((2, 4, 7, 5))
+    k = RNG.standard_normal((2, 2, 7, 5))
+    lse = oracle.attention_lse(q, k, causal=True)
+    for b, h in itertools.product(range(2), range(4)):
+        s = q[b, h] @ k[b, h // 2].T / math.sqrt(5)
+        s = np.where(np.tril(np.ones((7, 7), dtype=bool)), s, -np.inf)
+        np.testing.assert_allclose(lse[b, h], scipy.special.logsumexp(s, axis=-1), rtol=1e-13)
+        np.testing.assert_allclose(np.exp(s - lse[b, h][:, None]).sum(-1), 1.0, rtol=1e-13)
+
+
+def test_lse_brute_force_small_shapes():
+    for (B, Hkv, G, Sq, Sk, D, causal) in [(1, 1, 1, 3, 5, 2, False), (2, 2, 2, 4, 4, 3, True), (1, 2, 2, 1, 5, 4, True)]:
+        q = RNG.standard_normal((B, Hkv * G, Sq, D))
+        k = RNG.standard_normal((B, Hkv, Sk, D))
+        want = np.array(brute.attention_lse(q.tolist(), k.tolist(), causal=causal))
+        np.testing.assert_allclose(oracle.attention_lse(q, k, causal=causal), want, rtol=1e-12, atol=1e-12)
+
+
+def test_lse_is_the_recurrence_final_state():
+    """The blockwise recurrence's last (m, l) gives m + log l = LSE (the state page P4 carries block to block)."""
+    q = RNG.standard_normal((5, 6))
+    k = RNG.standard_normal((70, 6))
+    v = RNG.standard_normal((70, 6))
+    _, traces = recurrence.attention_blockwise(q, k, v, block=32, trace=True)
+    lse = oracle.attention_lse(q[None, None], k[None, None])[0, 0]
+    for i, hist in enumerate(traces):
+        m, l, _ = hist[-1]
+        assert abs(m + math.log(l) - lse[i]) < 1e-12
