@@ -130,47 +130,77 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
   const int grp = wave / kGroupWaves, wq = wave % kGroupWaves;
   const int l32 = lane & 31, hf = lane >> 5;
 
-  // ---- work decomposition (consecutive workgroups share the q tile and walk
-  // (batch, KV head); the 8 XCDs then each keep a fixed set of KV heads) ----
-  int qt = blockIdx.x / units_per_tile;
-  const int rem = blockIdx.x - qt * units_per_tile;
-  if (causal) qt = n_qtiles - 1 - qt;  // heaviest tiles first
+  // ---- work decomposition ----
+  // Tiles (a row tile of hp query heads of one KV head) are numbered tile =
+  // qt * units_per_tile + (batch, KV head, head group), with qt reversed when
+  // causal so the list runs heaviest first.  The launch has one workgroup per
+  // CU (or fewer when there are fewer tiles); workgroup w takes tile
+  // r * W + w in even rounds r and r * W + (W - 1 - w) in odd ones, so heavy
+  // and light causal tiles pair up.  Consecutive workgroups of a round walk
+  // (batch, KV head), so each XCD keeps a fixed set of KV heads.
   const int G = Hq / Hkv;
-  const int b = rem / (Hkv * n_hgroups);
-  const int kvh = (rem / n_hgroups) % Hkv;
-  const int hg = rem % n_hgroups;
+  const int W = gridDim.x;
+  const int n_tiles = n_qtiles * units_per_tile;
   const int rs = kGroupWaves / hp;  // 32-row tiles per group and head
-  const int head = kvh * G + hg * hp + (wq % hp);
   const int wg_rows = 2 * kRowsPerWave * rs;
-  const int wg_row0 = qt * wg_rows;
-  const int row0 = wg_row0 + (grp * rs + wq / hp) * kRowsPerWave;
-  const int q = row0 + l32;
-
-  const size_t q_base = (size_t)(b * Hq + head) * Sq * D;
-  const size_t kv_base = (size_t)(b * Hkv + kvh) * Sk * D;
-  // Rows past Sq (queries) or Sk (keys) read as zeros.
-  const __amdgpu_buffer_rsrc_t qr = make_rsrc(Qg + q_base, (uint32_t)Sq * D * 2);
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc(Kg + kv_base, (uint32_t)Sk * D * 2);
-  const __amdgpu_buffer_rsrc_t vr = make_rsrc(Vg + kv_base, (uint32_t)Sk * D * 2);
-
-  // ---- Q as the B operand: lane (query l32, half hf) holds d = 16kc + 8hf .. +8 ----
-  bf16x8 qreg[T::KC];
-#pragma unroll
-  for (int kc = 0; kc < T::KC; ++kc)
-    qreg[kc] = __builtin_bit_cast(bf16x8, buf_ld16(qr, (uint32_t)(q * D + kc * 16 + hf * 8) * 2));
-
-  // ---- key range ----
-  int wg_row_end = wg_row0 + wg_rows;
-  if (wg_row_end > Sq) wg_row_end = Sq;
   const bool cmask = causal && Sq > 1;
-  const int n_keys = cmask ? (wg_row_end < Sk ? wg_row_end : Sk) : Sk;
-  const int nblk = (n_keys + BN - 1) / BN;  // >= 1: the workgroup's first row exists and sees key 0
-  const bool wave_live = row0 < Sq;
-  const int wave_row_last = row0 + kRowsPerWave - 1;
-  // Does this wavefront's work include block j?  (Blocks wholly after its rows do not.)
+  auto tile_index = [&](int r) {
+    const int w = (r & 1) ? W - 1 - (int)blockIdx.x : (int)blockIdx.x;
+    const int idx = r * W + w;
+    return idx < n_tiles ? idx : -1;
+  };
+  auto tile_qt = [&](int idx) {
+    const int qt = idx / units_per_tile;
+    return causal ? n_qtiles - 1 - qt : qt;
+  };
+  auto tile_nblk = [&](int idx) {
+    int end = tile_qt(idx) * wg_rows + wg_rows;
+    if (end > Sq) end = Sq;
+    const int n_keys = cmask ? (end < Sk ? end : Sk) : Sk;
+    return (n_keys + BN - 1) / BN;  // >= 1: the tile's first row exists and sees key 0
+  };
+  auto tile_kv_base = [&](int idx) {
+    const int rem = idx % units_per_tile;
+    return (size_t)((rem / (Hkv * n_hgroups)) * Hkv + (rem / n_hgroups) % Hkv) * Sk * D;
+  };
+
+  // The tile whose rows this wavefront is computing: its query head and rows.
+  int head = 0, row0 = 0, q = 0, nblk = 1, wave_row_last = 0;
+  bool wave_live = false;
+  size_t q_base = 0;
+  auto enter_tile = [&](int idx) __attribute__((always_inline)) {
+    const int qt = tile_qt(idx);
+    const int rem = idx % units_per_tile;
+    const int b = rem / (Hkv * n_hgroups);
+    const int kvh = (rem / n_hgroups) % Hkv;
+    const int hg = rem % n_hgroups;
+    head = b * Hq + kvh * G + hg * hp + (wq % hp);  // (batch, query head) flattened
+    row0 = qt * wg_rows + (grp * rs + wq / hp) * kRowsPerWave;
+    q = row0 + l32;
+    nblk = tile_nblk(idx);
+    wave_live = row0 < Sq;
+    wave_row_last = row0 + kRowsPerWave - 1;
+    q_base = (size_t)head * Sq * D;
+  };
+  // Does this wavefront's work include block j of its tile?  (Blocks wholly
+  // after its rows do not.)
   auto visible = [&](int j) { return wave_live && j < nblk && (!cmask || j * BN <= wave_row_last); };
   // Does block j need the mask for some row of this wavefront?
   auto needs_mask = [&](int j) { return j * BN + BN > Sk || (cmask && j * BN + BN - 1 > row0); };
+
+  // ---- Q as the B operand: lane (query l32, half hf) holds d = 16kc + 8hf .. +8 ----
+  // Rows past Sq read as zeros.
+  bf16x8 qreg[T::KC];
+  auto load_q = [&](int idx) __attribute__((always_inline)) {
+    const int qt = tile_qt(idx);
+    const int rem = idx % units_per_tile;
+    const int hq = (rem / (Hkv * n_hgroups)) * Hq + ((rem / n_hgroups) % Hkv) * G + (rem % n_hgroups) * hp + (wq % hp);
+    const int qq = qt * wg_rows + (grp * rs + wq / hp) * kRowsPerWave + l32;
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(Qg + (size_t)hq * Sq * D, (uint32_t)Sq * D * 2);
+#pragma unroll
+    for (int kc = 0; kc < T::KC; ++kc)
+      qreg[kc] = __builtin_bit_cast(bf16x8, buf_ld16(qr, (uint32_t)(qq * D + kc * 16 + hf * 8) * 2));
+  };
 
   // ---- global -> LDS staging with buffer_load_dwordx4 ... lds ----
   // A direct-to-LDS load writes lane i's 16 bytes at M0 + 16 i, so each lane
@@ -183,33 +213,50 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
   const int dma_row0 = wave * T::LDS_ROWS + dma_row;
   const int k_voff = (dma_row0 * D + ((dma_chunk ^ k_swz<T::CH>(dma_row0)) << 3)) * 2;
   const int v_voff = (dma_row0 * D + ((dma_chunk ^ v_swz<T::CH>(dma_row0)) << 3)) * 2;
-  auto dma_one = [&](__amdgpu_buffer_rsrc_t rsrc, int voff, int j0, unsigned char* dst, int r) {
+  auto dma_one = [&](const uint16_t* base, int voff, int j0, unsigned char* dst, int r) __attribute__((always_inline)) {
+    // Rows past Sk read as zeros (buffer resource bound).
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(base, (uint32_t)Sk * D * 2);
     const int inst = r * kPrefillWaves + wave;  // uniform
+    // (soffset goes through a local: written inline as the builtin's argument,
+    // this expression kept the host compiler from emitting the launch stub.)
     const int soff = (j0 + r * kPrefillWaves * T::LDS_ROWS) * D * 2;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(dst + inst * 1024), 16,
                                              voff, soff, 0, 0);
   };
-  auto dma_block = [&](__amdgpu_buffer_rsrc_t rsrc, int voff, int j0, unsigned char* dst) {
+  // The load stream walks the workgroup's blocks (all its tiles, in order)
+  // ahead of the compute: cursor v at the block whose V is loaded next, cursor
+  // k one block further (its K is loaded with that V).  Past the last block
+  // the cursors keep stepping through the last tile (rows past the end read as
+  // zeros or are never used), so every phase issues the same loads.
+  struct Cursor {
+    int r, j, nblk;
+    size_t kv_base;
+  };
+  auto cursor_at = [&](int r) {
+    const int idx = tile_index(r);
+    return Cursor{r, 0, tile_nblk(idx), tile_kv_base(idx)};
+  };
+  auto advance = [&](Cursor& cu) __attribute__((always_inline)) {
+    if (++cu.j == cu.nblk && tile_index(cu.r + 1) >= 0) cu = cursor_at(cu.r + 1);
+  };
+  Cursor cur_v = cursor_at(0), cur_k = cursor_at(0);
+  // Stage s: V of the block at cursor v and K of the block at cursor k (the
+  // block after it), then both cursors step on.  Every stage is issued whole,
+  // so each phase issues a fixed number of loads and every wait below has a
+  // fixed count; the compiler can then tell which loads have landed.
+  auto load_k_only = [&](int stage) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < T::DMA_PER_WAVE; ++r) dma_one(Kg + cur_k.kv_base, k_voff, cur_k.j * BN, k_stage[stage], r);
+    advance(cur_k);
+  };
+  auto load_stage = [&](int stage) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < T::DMA_PER_WAVE; ++r) {
-      const int inst = r * kPrefillWaves + wave;  // uniform
-      // (soffset goes through a local: written inline as the builtin's
-      // argument, this expression kept the host compiler from emitting the
-      // kernel's launch stub.)
-      const int soff = (j0 + r * kPrefillWaves * T::LDS_ROWS) * D * 2;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(dst + inst * 1024),
-                                               16, voff, soff, 0, 0);
+      dma_one(Vg + cur_v.kv_base, v_voff, cur_v.j * BN, v_stage[stage % kStages], r);
+      dma_one(Kg + cur_k.kv_base, k_voff, cur_k.j * BN, k_stage[stage % kStages], r);
     }
-  };
-  // Stage of block j: K of block j+1 and V of block j.  Every stage is issued
-  // whole, also past the last block (those rows read as zeros or are never
-  // used), so each phase issues a fixed number of loads and every wait below
-  // has a fixed count; the compiler can then tell which loads have landed.
-  auto load_k = [&](int j0, unsigned char* dst) { dma_block(kr, k_voff, j0, dst); };
-  auto load_v = [&](int j0, unsigned char* dst) { dma_block(vr, v_voff, j0, dst); };
-  auto load_stage = [&](int stage, int j) {
-    load_k((j + 1) * BN, k_stage[stage % kStages]);
-    load_v(j * BN, v_stage[stage % kStages]);
+    advance(cur_v);
+    advance(cur_k);
   };
   constexpr int kStageLoads = 2 * T::DMA_PER_WAVE;  // per wavefront
   static_assert(kStageLoads < 16, "vmcnt immediate");
@@ -252,7 +299,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
   bf16x8 pb[2][2];  // its bf16 weights, the B operand of the next PV
 
   // S^T = K Q^T for one block: two 32-key sub-tiles.
-  auto qk = [&](const unsigned char* kl) {
+  auto qk = [&](const unsigned char* kl) __attribute__((always_inline)) {
     s[0] = f32x16{};
     s[1] = f32x16{};
 #pragma unroll
@@ -267,12 +314,13 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
 
   // MFMA phase: scores of the next block (K in kl), O^T += V^T P^T for this
   // block (V in vl; the A operand is 8 keys of column d, from two transposed
-  // reads) and the loads of stage `jn` into k_dst / v_dst.  The order is fixed by
+  // reads) and the next stage's loads (at the load cursors) into k_dst /
+  // v_dst.  The order is fixed by
   // hand (sched_barrier fences): the LDS read of each MFMA's fragment is
   // issued kAhead MFMAs earlier, into a ring of registers, and the loads of
   // the later stage are spread over the score MFMAs.
   auto gemm_fast = [&](const unsigned char* kl, const unsigned char* vl, unsigned char* k_dst,
-                       unsigned char* v_dst, int jn) {
+                       unsigned char* v_dst) __attribute__((always_inline)) {
     constexpr int NQ = 2 * T::KC, NP = 4 * T::DT, N = NQ + NP;
     constexpr int kAhead = 6, kRing = 8;
     auto frag = [&](int m) -> bf16x8 {
@@ -306,8 +354,8 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
         if (m % kDmaEvery == kDmaEvery - 1) {  // one direct-to-LDS load of stage jn
           const int d = m / kDmaEvery;           // 0 .. 2 * DMA_PER_WAVE - 1
           const int r = d % T::DMA_PER_WAVE;
-          if (d < T::DMA_PER_WAVE) dma_one(kr, k_voff, (jn + 1) * BN, k_dst, r);
-          else dma_one(vr, v_voff, jn * BN, v_dst, r);
+          if (d < T::DMA_PER_WAVE) dma_one(Kg + cur_k.kv_base, k_voff, cur_k.j * BN, k_dst, r);
+          else dma_one(Vg + cur_v.kv_base, v_voff, cur_v.j * BN, v_dst, r);
         }
       } else {
         const int i = m - NQ;
@@ -321,7 +369,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
   // Softmax of block j (scores in s): mask, running max and lazy rescale,
   // exponentials and bf16 weights into pb (their row sums are taken with the
   // PV on the matrix cores).
-  auto softmax = [&](int j) {
+  auto softmax = [&](int j) __attribute__((always_inline)) {
     const int j0 = j * BN;
     if (needs_mask(j)) {
       // key j0 + 4hf + o is visible iff o < lim, o = 32t + 8(r/4) + r%4
@@ -367,82 +415,125 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
       }
   };
 
-  // Block j at stage P = j mod 4.  MFMA phase: scores of block j+1 (K in stage
-  // P) and O += P V for block j (V in stage P).  Softmax phase: load stage
-  // P+3 (block j+3), softmax of block j+1, then wait for this wavefront's
-  // older loads (stage P+2 and before) so that after the barrier they are
-  // visible to all.
-  auto block = [&](int P, int j) {
+  // ---- epilogue of a tile: O = acc / l (bf16, round to nearest even) and, if
+  // asked, the log-sum-exp ln 2 * (m + log2 l): the sum of 2^(s c) is 2^m l for
+  // whatever reference m the row ended with ----
+  auto store_tile = [&]() __attribute__((always_inline)) {
+    const float l_tot = acc_l[0];
+    const float inv = 1.0f / l_tot;
+    if (Lse && hf == 0 && q < Sq) Lse[(size_t)head * Sq + q] = (m_ref + log2f(l_tot)) * kLn2;
+    if (q < Sq) {
+      uint16_t* op = Og + q_base + (size_t)q * D;
+#pragma unroll
+      for (int dt = 0; dt < T::DT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * dt + 8 * g + 4 * hf;
+          const u32x2 w = {pack_bf16x2(acc[dt][4 * g] * inv, acc[dt][4 * g + 1] * inv),
+                           pack_bf16x2(acc[dt][4 * g + 2] * inv, acc[dt][4 * g + 3] * inv)};
+          *reinterpret_cast<u32x2*>(op + d0) = w;
+        }
+    }
+  };
+
+  // The block the next softmax phase handles: block jc of tile rc (ordinal
+  // among this workgroup's tiles).
+  int rc = 0, jc = 0;
+  bool finished = false;
+  // Softmax phase.  With `next`, it moves to the following block first; when
+  // that starts a new tile, the finished tile is stored (its last PV was
+  // issued in the MFMA phase just ended) and the running state restarts (the
+  // first visible block rescales acc and l by 2^-inf = 0).  When the block is
+  // the last of its tile, the next tile's Q is loaded here, for the scores the
+  // next MFMA phase computes.  Ends by waiting for this wavefront's loads of
+  // the stage two blocks ahead (and for Q, when it was loaded).
+  auto softmax_phase = [&](bool next) __attribute__((always_inline)) {
+    if (next) {
+      if (jc + 1 < nblk) {
+        ++jc;
+      } else {
+        store_tile();
+        const int idx = tile_index(rc + 1);
+        if (idx < 0) {
+          finished = true;
+        } else {
+          ++rc;
+          jc = 0;
+          enter_tile(idx);
+          m_ref = kNegInf;
+        }
+      }
+    }
+    auto weights = [&]() __attribute__((always_inline)) {
+      if (!finished && visible(jc)) {
+        softmax(jc);
+      } else {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) pb[t][u] = bf16x8{};
+      }
+    };
+    // The next tile's Q is waited for right after its load, in the same
+    // branch: the compiler then knows on every path that Q has landed and adds
+    // no waits before the score MFMAs (once per tile, the load latency shows).
+    const int next_q = !finished && jc + 1 == nblk ? tile_index(rc + 1) : -1;
+    if (next_q >= 0) {
+      load_q(next_q);
+      wait_vmcnt<0>();
+    }
+    weights();
+    wait_vmcnt<kStageLoads>();
+  };
+
+  // Global block g at stage P = g mod 4 (g counts the blocks of all this
+  // workgroup's tiles).  MFMA phase: scores of block g+1 (K in stage P), O += P V
+  // for block g (V in stage P), loads of stage P+3 (V of block g+3, K of block
+  // g+4).  Softmax phase: block g+1.
+  auto block = [&](int P) __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(2);  // the MFMA phase wins issue slots over the other group's softmax
     // Always the full MFMA phase: a block this wavefront cannot see has zero
     // weights (its PV adds nothing) and its scores go unused.
-    gemm_fast(k_stage[P], v_stage[P], k_stage[(P + 3) % kStages], v_stage[(P + 3) % kStages], j + 3);
+    gemm_fast(k_stage[P], v_stage[P], k_stage[(P + 3) % kStages], v_stage[(P + 3) % kStages]);
+    advance(cur_v);
+    advance(cur_k);
     phase_barrier();
     __builtin_amdgcn_s_setprio(0);
-    if (visible(j + 1)) {
-      softmax(j + 1);
-    } else {
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) pb[t][u] = bf16x8{};
-    }
-    wait_vmcnt<kStageLoads>();
+    softmax_phase(true);
     phase_barrier();
   };
 
-  // ---- prologue: K of block 0 into stage 3, stages 0..2; scores and softmax of block 0 ----
+  // ---- prologue: Q of the first tile; K of block 0 into stage 3, stages 0..2;
+  // scores and softmax of block 0 ----
+  int n_blocks = 0;  // blocks of all this workgroup's tiles
+  for (int r = 0; tile_index(r) >= 0; ++r) n_blocks += tile_nblk(tile_index(r));
+  enter_tile(tile_index(0));
+  load_q(tile_index(0));
+  load_k_only(3);
+  load_stage(0);
+  load_stage(1);
+  load_stage(2);
   // Stage 1 is read in the third phase, before group B's first wait; so only
   // stage 2 may still be in flight at the first barrier.
-  load_k(0, k_stage[3]);
-  load_stage(0, 0);
-  load_stage(1, 1);
-  load_stage(2, 2);
   wait_vmcnt<kStageLoads>();
   phase_barrier();
-  if (visible(0)) {
-    qk(k_stage[3]);
-    softmax(0);
-  } else {
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) pb[t][u] = bf16x8{};
-  }
+  qk(k_stage[3]);
+  softmax_phase(false);
   phase_barrier();
   if (grp == 1) phase_barrier();  // group B runs one phase behind group A
 
-  int j = 0;
-  for (; j + kStages <= nblk; j += kStages) {
-    block(0, j);
-    block(1, j + 1);
-    block(2, j + 2);
-    block(3, j + 3);
+  int g = 0;
+  for (; g + kStages <= n_blocks; g += kStages) {
+    block(0);
+    block(1);
+    block(2);
+    block(3);
   }
-  if (j < nblk) block(0, j);
-  if (j + 1 < nblk) block(1, j + 1);
-  if (j + 2 < nblk) block(2, j + 2);
+  if (g < n_blocks) block(0);
+  if (g + 1 < n_blocks) block(1);
+  if (g + 2 < n_blocks) block(2);
   if (grp == 0) phase_barrier();  // group A ends one phase ahead: keep the barrier counts equal
   wait_vmcnt<0>();  // no load into LDS may land after the workgroup has ended
-
-  // ---- epilogue: O = acc / l, bf16 round-to-nearest-even ----
-  const float l_tot = acc_l[0];
-  const float inv = 1.0f / l_tot;
-  // log sum_j exp(scale * s_j) = ln 2 * (m + log2 l): the sum of 2^(s c) is 2^m l
-  // for whatever reference m the row ended with.
-  if (Lse && hf == 0 && q < Sq) Lse[(size_t)(b * Hq + head) * Sq + q] = (m_ref + log2f(l_tot)) * kLn2;
-  if (q < Sq) {
-    uint16_t* op = Og + q_base + (size_t)q * D;
-#pragma unroll
-    for (int dt = 0; dt < T::DT; ++dt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * dt + 8 * g + 4 * hf;
-        const u32x2 w = {pack_bf16x2(acc[dt][4 * g] * inv, acc[dt][4 * g + 1] * inv),
-                         pack_bf16x2(acc[dt][4 * g + 2] * inv, acc[dt][4 * g + 3] * inv)};
-        *reinterpret_cast<u32x2*>(op + d0) = w;
-      }
-  }
 }
 
 template <int D>
@@ -453,7 +544,14 @@ hipError_t launch(const AttnArgs& a) {
   const int rows_per_wg = a.plan.block_m;
   const int n_qtiles = (a.seq_q + rows_per_wg - 1) / rows_per_wg;
   const int units_per_tile = a.batch * a.heads_kv * n_hgroups;
-  hipLaunchKernelGGL(prefill_bf16_kernel<D>, dim3((unsigned)a.plan.grid), dim3(kPrefillThreads), 0, a.stream,
+  // One persistent workgroup per CU (fewer when there are fewer tiles); they
+  // walk the plan's tiles.
+  int dev = 0, n_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int64_t grid = a.plan.grid < n_cu ? a.plan.grid : n_cu;
+  hipLaunchKernelGGL(prefill_bf16_kernel<D>, dim3((unsigned)grid), dim3(kPrefillThreads), 0, a.stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse, a.heads_q, a.heads_kv,
                      a.seq_q, a.seq_k, a.causal, a.c, hp, n_hgroups, n_qtiles, units_per_tile);

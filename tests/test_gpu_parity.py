@@ -133,6 +133,12 @@ PREFILL_CASES = [
     ("bf16", 1, 8, 1, 97, 97, 128, True),       # G=8: two head groups
     ("bf16", 1, 2, 1, 1, 77, 128, False),       # Sq=1 through the decode path
     ("bf16", 1, 40, 2, 1, 300, 128, True),      # G=20 > 16: Sq=1 falls back to the prefill kernel
+    # more row tiles than CUs: persistent workgroups walk several tiles, the
+    # load stream and the scores run across tile boundaries
+    ("bf16", 8, 32, 8, 257, 257, 128, True),    # 320 tiles of 64 rows (G=4)
+    ("bf16", 16, 16, 8, 300, 300, 128, False),  # 384 tiles of 128 rows (G=2)
+    ("bf16", 20, 32, 8, 100, 100, 64, True),    # 320 tiles of 1 and 2 key blocks, D=64
+    ("bf16", 3, 96, 96, 130, 130, 64, True),    # 288 MHA tiles of 256 rows, one key block each
     ("f32", 1, 1, 1, 65, 257, 48, False),
     ("f32", 1, 2, 1, 100, 100, 128, True),
     ("f32", 2, 4, 2, 33, 90, 4, False),
