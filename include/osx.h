@@ -140,6 +140,26 @@ int osx_softmax_rows_workspace(int64_t rows, int64_t cols, size_t* bytes);
 int osx_softmax_rows(const float* x, float* y, int64_t rows, int64_t cols, void* workspace, size_t workspace_bytes,
                      void* stream);
 
+/*
+ * osx_softmax_rows_ex -- osx_softmax_rows with options:
+ *     y[r, c] = exp(scale x[r, c]) / sum_{c' visible} exp(scale x[r, c'])
+ * for visible c, and y[r, c] = 0 for masked c.
+ *
+ * dtype: OSX_F32 or OSX_BF16, the element type of both x and y (bf16 values
+ * are read exactly and y is rounded to nearest even; the arithmetic is fp32).
+ * causal_period: 0 for no mask; P > 0 keeps, in row r, the columns
+ * c <= r mod P (x is a stack of [P, cols] score matrices, one per head, and
+ * the mask is page "从零开始写Qwen3（五-其一）使用Triton实现自注意力", section
+ * softmax的triton实现: column <= row, the rest loaded as -inf).  Every row
+ * keeps column 0.  Masked columns of x are not read.
+ * scale: positive and finite (1 for none); it multiplies x before the
+ * softmax (the attention scale d^-1/2 of page "softmax_attention").
+ * workspace: as for osx_softmax_rows (osx_softmax_rows_workspace gives the
+ * size; it does not depend on dtype, mask or scale).  x == y is allowed.
+ */
+int osx_softmax_rows_ex(const void* x, void* y, int dtype, int64_t rows, int64_t cols, int64_t causal_period,
+                        float scale, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* osx_status_string(int status);
 

@@ -59,13 +59,14 @@ def _load() -> ctypes.CDLL:
     lib.osx_softmax_rows_plan.argtypes = [_i64, _i64, ctypes.POINTER(Plan)]
     lib.osx_softmax_rows_workspace.argtypes = [_i64, _i64, ctypes.POINTER(_sz)]
     lib.osx_softmax_rows.argtypes = [_vp, _vp, _i64, _i64, _vp, _sz, _vp]
+    lib.osx_softmax_rows_ex.argtypes = [_vp, _vp, _i, _i64, _i64, _i64, _f, _vp, _sz, _vp]
     lib.osx_status_string.argtypes = [_i]
     lib.osx_status_string.restype = ctypes.c_char_p
     lib.osx_last_error.argtypes = []
     lib.osx_last_error.restype = ctypes.c_char_p
     lib.osx_version.argtypes = []
     for name in ("osx_attn_plan", "osx_attn_fwd_workspace", "osx_attn_fwd", "osx_attn_fwd_lse", "osx_softmax_rows_plan",
-                 "osx_softmax_rows_workspace", "osx_softmax_rows", "osx_version"):
+                 "osx_softmax_rows_workspace", "osx_softmax_rows", "osx_softmax_rows_ex", "osx_version"):
         getattr(lib, name).restype = _i
     return lib
 
@@ -192,14 +193,16 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None
     return out, lse
 
 
-def softmax_rows(x, out=None, workspace=None, stream=None):
-    """y = softmax(x) along the last dimension of a contiguous float32 CUDA tensor (2-D or 1-D).
+def softmax_rows(x, out=None, workspace=None, stream=None, causal_period: int = 0, scale: float = 1.0):
+    """y = softmax(scale * x) along the last dimension of a contiguous float32 or bfloat16 CUDA tensor.
 
-    ``out`` may be ``x`` itself (in place).
+    ``causal_period`` P > 0 masks, in row r (of the rows flattened to 2-D),
+    the columns c > r mod P (y = 0 there).  ``out`` may be ``x`` itself (in
+    place); y has x's dtype.
     """
     torch = _torch()
-    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
-        raise ValueError("x must be a contiguous float32 CUDA tensor")
+    if x.dtype not in (torch.float32, torch.bfloat16) or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous float32 or bfloat16 CUDA tensor")
     cols = x.shape[-1] if x.dim() else 1
     rows = x.numel() // cols if cols else 0
     if out is None:
@@ -211,7 +214,11 @@ def softmax_rows(x, out=None, workspace=None, stream=None):
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(lib.osx_softmax_rows(x.data_ptr(), out.data_ptr(), rows, cols, ws_ptr, ws_len, _stream(x, stream)))
+    if x.dtype == torch.float32 and not causal_period and scale == 1.0:
+        _check(lib.osx_softmax_rows(x.data_ptr(), out.data_ptr(), rows, cols, ws_ptr, ws_len, _stream(x, stream)))
+    else:
+        _check(lib.osx_softmax_rows_ex(x.data_ptr(), out.data_ptr(), _dtype_code(x), rows, cols, int(causal_period),
+                                       float(scale), ws_ptr, ws_len, _stream(x, stream)))
     return out
 
 

@@ -239,14 +239,21 @@ int osx_softmax_rows_workspace(int64_t rows, int64_t cols, size_t* bytes) {
   return st;
 }
 
-int osx_softmax_rows(const float* x, float* y, int64_t rows, int64_t cols, void* workspace, size_t workspace_bytes,
-                     void* stream) {
+}  // extern "C"
+
+namespace {
+
+int softmax_rows(const void* x, void* y, int dtype, int64_t rows, int64_t cols, int64_t causal_period, float scale,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != OSX_F32 && dtype != OSX_BF16) return fail(OSX_EINVAL, "dtype %d: OSX_F32 or OSX_BF16", dtype);
+  if (causal_period < 0) return fail(OSX_EINVAL, "negative causal_period %lld", (long long)causal_period);
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(OSX_EINVAL, "scale must be positive and finite");
   osx_plan p;
   int st = plan_softmax(rows, cols, &p);
   if (st != OSX_OK) return st;
   if (p.kernel == OSX_KERNEL_NONE) return ok();
   if (!x || !y) return fail(OSX_EINVAL, "null x or y pointer");
-  const size_t n = (size_t)rows * (size_t)cols * sizeof(float);
+  const size_t n = (size_t)rows * (size_t)cols * (dtype == OSX_BF16 ? 2 : 4);
   if (x != y && overlap(x, n, y, n)) return fail(OSX_EINVAL, "x and y overlap without being the same buffer");
   if (p.workspace_bytes > 0 && (!workspace || workspace_bytes < p.workspace_bytes))
     return fail(OSX_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : (size_t)0,
@@ -256,8 +263,11 @@ int osx_softmax_rows(const float* x, float* y, int64_t rows, int64_t cols, void*
   osx::SoftmaxArgs a;
   a.x = x;
   a.y = y;
+  a.dtype = dtype;
   a.rows = rows;
   a.cols = cols;
+  a.k = (float)((double)scale * 1.4426950408889634);
+  a.period = causal_period;
   a.workspace = workspace;
   a.stream = (hipStream_t)stream;
   a.plan = p;
@@ -265,6 +275,20 @@ int osx_softmax_rows(const float* x, float* y, int64_t rows, int64_t cols, void*
   if (e == hipSuccess) e = hipGetLastError();
   if (e != hipSuccess) return fail(OSX_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int osx_softmax_rows(const float* x, float* y, int64_t rows, int64_t cols, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  return softmax_rows(x, y, OSX_F32, rows, cols, 0, 1.0f, workspace, workspace_bytes, stream);
+}
+
+int osx_softmax_rows_ex(const void* x, void* y, int dtype, int64_t rows, int64_t cols, int64_t causal_period,
+                        float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  return softmax_rows(x, y, dtype, rows, cols, causal_period, scale, workspace, workspace_bytes, stream);
 }
 
 const char* osx_status_string(int status) {

@@ -41,9 +41,12 @@ struct AttnArgs {
 };
 
 struct SoftmaxArgs {
-  const float* x;
-  float* y;
+  const void* x;
+  void* y;
+  int dtype;       // OSX_F32 or OSX_BF16, for x and y
   int64_t rows, cols;
+  float k;         // scale * log2(e): y = 2^((x - max) k) / sum
+  int64_t period;  // causal period (row r keeps columns <= r mod period), 0 = no mask
   void* workspace;
   hipStream_t stream;
   osx_plan plan;

@@ -1,12 +1,19 @@
-// Two-pass row softmax for gfx950.
+// Two-pass row softmax for gfx950: y = softmax(scale * x) along each row,
+// optionally with a causal mask, fp32 or bf16 in and out (fp32 arithmetic).
 //
 // Pass 1 keeps an online state per thread -- the running max m and the sum l
-// of exp(x - m) -- rescaling l by exp(m_old - m_new) whenever the max grows,
-// then merges the per-thread states across the wavefront and the workgroup
-// (page "Softmax 算子的实现与优化", section Online Softmax: the boxed update
-// and the invariant l = sum_j e^{x_j - m}).  Pass 2 reads x again and writes
-// y = exp(x - m) / l.  Out-of-range positions contribute nothing (-inf to the
-// max, 0 to the sum).
+// of exp(scale (x - m)) -- rescaling l by exp(scale (m_old - m_new)) whenever
+// the max grows, then merges the per-thread states across the wavefront and
+// the workgroup (page "Softmax 算子的实现与优化", section Online Softmax: the
+// boxed update and the invariant l = sum_j e^{x_j - m}).  Pass 2 reads x again
+// and writes y = exp(scale (x - m)) / l.  Out-of-range positions contribute
+// nothing (-inf to the max, 0 to the sum).
+//
+// Causal mask (page "从零开始写Qwen3（五-其一）使用Triton实现自注意力", section
+// softmax的triton实现: keep column <= row, the rest counts as -inf): for a
+// causal period P > 0, row r keeps columns c <= r mod P, i.e. the rows are
+// stacked [P, cols] score matrices of several heads.  Masked columns are never
+// read; they are written as 0.
 //
 // Two shapes of launch:
 //  * rows up to kSoftmaxRowMax elements: one workgroup per row does both
@@ -16,7 +23,8 @@
 //    a row's partials with the same rescaling rule, then normalises its chunk.
 //    This replaces the single-program scan, which cannot use more than one CU.
 //
-// Exponentials are 2^((x - m) * log2 e) on the transcendental unit.
+// Exponentials are 2^((x - m) * k) with k = scale * log2 e, on the
+// transcendental unit.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -26,21 +34,68 @@ namespace {
 constexpr int kThreads = kSoftmaxThreads;
 constexpr int kWaves = kThreads / kWaveSize;
 
-// Natural-units online state: l = sum exp(x - m) over the elements seen.
+// Element types: fp32, or bf16 held as its 16-bit pattern.  A 16-byte vector
+// holds E elements.
+template <typename T>
+struct Elem;
+template <>
+struct Elem<float> {
+  static constexpr int E = 4;
+  static __device__ __forceinline__ float get(const float* p) { return *p; }
+  static __device__ __forceinline__ void put(float* p, float v) { *p = v; }
+  // The whole vector is bit-cast: ROCm 7.2 clang lowers a bit-cast of one
+  // ext-vector component (w.y) as a load from the vector's first element.
+  static __device__ __forceinline__ void unpack(u32x4 w, float (&v)[E]) {
+    const f32x4 f = __builtin_bit_cast(f32x4, w);
+    v[0] = f.x;
+    v[1] = f.y;
+    v[2] = f.z;
+    v[3] = f.w;
+  }
+  static __device__ __forceinline__ u32x4 pack(const float (&v)[E]) {
+    return __builtin_bit_cast(u32x4, f32x4{v[0], v[1], v[2], v[3]});
+  }
+};
+template <>
+struct Elem<uint16_t> {
+  static constexpr int E = 8;
+  static __device__ __forceinline__ float get(const uint16_t* p) { return bf16_lo((uint32_t)*p); }
+  static __device__ __forceinline__ void put(uint16_t* p, float v) { *p = (uint16_t)(pack_bf16x2(v, 0.f) & 0xffffu); }
+  static __device__ __forceinline__ void unpack(u32x4 w, float (&v)[E]) {
+    v[0] = bf16_lo(w.x);
+    v[1] = bf16_hi(w.x);
+    v[2] = bf16_lo(w.y);
+    v[3] = bf16_hi(w.y);
+    v[4] = bf16_lo(w.z);
+    v[5] = bf16_hi(w.z);
+    v[6] = bf16_lo(w.w);
+    v[7] = bf16_hi(w.w);
+  }
+  static __device__ __forceinline__ u32x4 pack(const float (&v)[E]) {
+    return u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ u32x4 ld16(const T* p) { return *reinterpret_cast<const u32x4*>(p); }
+template <typename T>
+__device__ __forceinline__ void st16(T* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// Online state: m is a max of x, l = sum 2^((x - m) k) over the elements seen.
 struct State {
   float m, l;
 };
 
-__device__ __forceinline__ void merge_state(State& s, float mb, float lb) {
+__device__ __forceinline__ void merge_state(State& s, float mb, float lb, float k) {
   const float mn = fmaxf(s.m, mb);
   if (mn == kNegInf) return;  // both empty
-  s.l = s.l * exp2_fast((s.m - mn) * kLog2e) + lb * exp2_fast((mb - mn) * kLog2e);
+  s.l = s.l * exp2_fast((s.m - mn) * k) + lb * exp2_fast((mb - mn) * k);
   s.m = mn;
 }
 
 // Fold a group of values into the state: one max over the group, one rescale.
 template <int N>
-__device__ __forceinline__ void update(State& s, const float (&v)[N]) {
+__device__ __forceinline__ void update(State& s, const float (&v)[N], float k) {
   float mb = v[0];
 #pragma unroll
   for (int i = 1; i < N; ++i) mb = fmaxf(mb, v[i]);
@@ -48,18 +103,18 @@ __device__ __forceinline__ void update(State& s, const float (&v)[N]) {
   if (mn == kNegInf) return;
   float sum = 0.f;
 #pragma unroll
-  for (int i = 0; i < N; ++i) sum += exp2_fast((v[i] - mn) * kLog2e);
-  s.l = s.l * exp2_fast((s.m - mn) * kLog2e) + sum;
+  for (int i = 0; i < N; ++i) sum += exp2_fast((v[i] - mn) * k);
+  s.l = s.l * exp2_fast((s.m - mn) * k) + sum;
   s.m = mn;
 }
 
 // Merge the states of all threads of the workgroup; every thread gets the result.
-__device__ __forceinline__ State block_merge(State s, float* sm /* 2*kWaves floats */) {
+__device__ __forceinline__ State block_merge(State s, float* sm /* 2*kWaves floats */, float k) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     const float mb = __shfl_xor(s.m, o, 64);
     const float lb = __shfl_xor(s.l, o, 64);
-    merge_state(s, mb, lb);
+    merge_state(s, mb, lb, k);
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) {
@@ -69,129 +124,178 @@ __device__ __forceinline__ State block_merge(State s, float* sm /* 2*kWaves floa
   __syncthreads();
   State r = {sm[0], sm[1]};
 #pragma unroll
-  for (int w = 1; w < kWaves; ++w) merge_state(r, sm[2 * w], sm[2 * w + 1]);
+  for (int w = 1; w < kWaves; ++w) merge_state(r, sm[2 * w], sm[2 * w + 1], k);
   return r;
 }
 
-__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
-__device__ __forceinline__ void st4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
-
-// Online pass over x[begin, end) of one row; VEC = 4 uses 16-byte loads
-// (begin, end multiples of 4, x 16-byte aligned).
-template <int VEC>
-__device__ __forceinline__ State scan(const float* __restrict__ x, int64_t begin, int64_t end) {
+// Online pass over x[begin, end) of one row.  VEC: 16-byte loads of E
+// elements (begin a multiple of E, x 16-byte aligned) plus a scalar tail.
+template <typename T, bool VEC>
+__device__ __forceinline__ State scan(const T* __restrict__ x, int64_t begin, int64_t end, float k) {
+  using L = Elem<T>;
+  constexpr int E = L::E;
   State s = {kNegInf, 0.f};
   const int tid = threadIdx.x;
-  if (VEC == 4) {
-    const int64_t n4 = (end - begin) >> 2;
-    const float* xb = x + begin;
+  int64_t tail = begin;
+  if (VEC && end > begin) {
+    const int64_t nv = (end - begin) / E;
+    const T* xb = x + begin;
     int64_t i = tid;
-    for (; i + 3 * kThreads < n4; i += 4 * kThreads) {
-      f32x4 a = ld4(xb + 4 * i), b = ld4(xb + 4 * (i + kThreads)), c = ld4(xb + 4 * (i + 2 * kThreads)),
-            d = ld4(xb + 4 * (i + 3 * kThreads));
-      const float v[16] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w, c.x, c.y, c.z, c.w, d.x, d.y, d.z, d.w};
-      update(s, v);
+    for (; i + kThreads < nv; i += 2 * kThreads) {
+      const u32x4 a = ld16(xb + E * i), b = ld16(xb + E * (i + kThreads));
+      float va[E], vb[E], v[2 * E];
+      L::unpack(a, va);
+      L::unpack(b, vb);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        v[e] = va[e];
+        v[E + e] = vb[e];
+      }
+      update(s, v, k);
     }
-    for (; i < n4; i += kThreads) {
-      f32x4 a = ld4(xb + 4 * i);
-      const float v[4] = {a.x, a.y, a.z, a.w};
-      update(s, v);
+    for (; i < nv; i += kThreads) {
+      float v[E];
+      L::unpack(ld16(xb + E * i), v);
+      update(s, v, k);
     }
-  } else {
-    for (int64_t i = begin + tid; i < end; i += kThreads) {
-      const float v[1] = {x[i]};
-      update(s, v);
-    }
+    tail = begin + nv * E;
+  }
+  for (int64_t i = tail + tid; i < end; i += kThreads) {
+    const float v[1] = {L::get(x + i)};
+    update(s, v, k);
   }
   return s;
 }
 
-// Normalise pass over [begin, end): y = 2^((x - m) log2 e) / l.
-template <int VEC>
-__device__ __forceinline__ void normalise(const float* __restrict__ x, float* __restrict__ y, int64_t begin,
-                                          int64_t end, float m, float inv_l) {
+// Normalise pass over [begin, end): y = 2^((x - m) k) * inv_l.
+template <typename T, bool VEC>
+__device__ __forceinline__ void normalise(const T* __restrict__ x, T* __restrict__ y, int64_t begin, int64_t end,
+                                          float m, float inv_l, float k) {
+  using L = Elem<T>;
+  constexpr int E = L::E;
   const int tid = threadIdx.x;
-  if (VEC == 4) {
-    const int64_t n4 = (end - begin) >> 2;
-    const float* xb = x + begin;
-    float* yb = y + begin;
-    for (int64_t i = tid; i < n4; i += kThreads) {
-      f32x4 a = ld4(xb + 4 * i);
-      f32x4 r;
-      r.x = exp2_fast((a.x - m) * kLog2e) * inv_l;
-      r.y = exp2_fast((a.y - m) * kLog2e) * inv_l;
-      r.z = exp2_fast((a.z - m) * kLog2e) * inv_l;
-      r.w = exp2_fast((a.w - m) * kLog2e) * inv_l;
-      st4(yb + 4 * i, r);
+  int64_t tail = begin;
+  if (VEC && end > begin) {
+    const int64_t nv = (end - begin) / E;
+    for (int64_t i = tid; i < nv; i += kThreads) {
+      float v[E];
+      L::unpack(ld16(x + begin + E * i), v);
+#pragma unroll
+      for (int e = 0; e < E; ++e) v[e] = exp2_fast((v[e] - m) * k) * inv_l;
+      st16(y + begin + E * i, L::pack(v));
     }
-  } else {
-    for (int64_t i = begin + tid; i < end; i += kThreads) y[i] = exp2_fast((x[i] - m) * kLog2e) * inv_l;
+    tail = begin + nv * E;
   }
+  for (int64_t i = tail + tid; i < end; i += kThreads) L::put(y + i, exp2_fast((L::get(x + i) - m) * k) * inv_l);
 }
 
-// A full chunk of kSoftmaxChunk elements, 16-byte loads: every thread issues
-// all of its kChunkVec loads before using any, so a workgroup keeps its whole
-// chunk in flight.  Thread state: its exact max, then the sum of
-// 2^((x - m) log2 e) over its values (the block-level merge is the rescaling
-// rule).  Pass 1 loads normally so x stays cached for pass 2; pass 2 is the
-// last use of x and streams y out with non-temporal accesses.
-constexpr int kChunkVec = (int)(kSoftmaxChunk / 4 / kThreads);  // float4 per thread per chunk
+// Masked columns [begin, end) of a row: y = 0.
+template <typename T, bool VEC>
+__device__ __forceinline__ void zero_fill(T* __restrict__ y, int64_t begin, int64_t end) {
+  using L = Elem<T>;
+  constexpr int E = L::E;
+  const int tid = threadIdx.x;
+  if (end <= begin) return;
+  int64_t head = end;  // scalar stores cover [begin, head)
+  if (VEC) {
+    head = (begin + E - 1) / E * E;  // the row starts 16-byte aligned, so this is too
+    if (head > end) head = end;
+    const int64_t nv = (end - head) / E;
+    for (int64_t i = tid; i < nv; i += kThreads) st16(y + head + E * i, u32x4{0u, 0u, 0u, 0u});
+    for (int64_t i = head + nv * E + tid; i < end; i += kThreads) L::put(y + i, 0.f);
+  }
+  for (int64_t i = begin + tid; i < head; i += kThreads) L::put(y + i, 0.f);
+}
 
-__device__ __forceinline__ State scan_chunk(const float* __restrict__ xb) {
-  f32x4 v[kChunkVec];
+// Visible columns of a row: all, or c <= row mod period.
+__device__ __forceinline__ int64_t row_limit(int64_t row, int64_t cols, int64_t period) {
+  if (period <= 0) return cols;
+  const int64_t lim = row % period + 1;
+  return lim < cols ? lim : cols;
+}
+
+// A full unmasked chunk of kSoftmaxChunk elements, 16-byte loads: every thread
+// issues all of its loads before using any, so a workgroup keeps its whole
+// chunk in flight.  Thread state: its exact max, then the sum of
+// 2^((x - m) k) over its values (the block-level merge is the rescaling rule).
+// Pass 1 loads normally so x stays cached for pass 2; pass 2 is the last use
+// of x and streams y out with non-temporal accesses.
+template <typename T>
+__device__ __forceinline__ State scan_chunk(const T* __restrict__ xb, float k) {
+  using L = Elem<T>;
+  constexpr int E = L::E, NV = (int)(kSoftmaxChunk / E / kThreads);
+  u32x4 w[NV];
 #pragma unroll
-  for (int i = 0; i < kChunkVec; ++i) v[i] = reinterpret_cast<const f32x4*>(xb)[threadIdx.x + i * kThreads];
-  float m = v[0].x;
+  for (int i = 0; i < NV; ++i) w[i] = ld16(xb + E * (threadIdx.x + i * kThreads));
+  float m = kNegInf;
 #pragma unroll
-  for (int i = 0; i < kChunkVec; ++i) m = fmaxf(fmaxf(m, fmaxf(v[i].x, v[i].y)), fmaxf(v[i].z, v[i].w));
+  for (int i = 0; i < NV; ++i) {
+    float v[E];
+    L::unpack(w[i], v);
+#pragma unroll
+    for (int e = 0; e < E; e += 2) m = fmaxf(m, fmaxf(v[e], v[e + 1]));
+  }
   float l = 0.f;
 #pragma unroll
-  for (int i = 0; i < kChunkVec; ++i)
-    l += (exp2_fast((v[i].x - m) * kLog2e) + exp2_fast((v[i].y - m) * kLog2e)) +
-         (exp2_fast((v[i].z - m) * kLog2e) + exp2_fast((v[i].w - m) * kLog2e));
+  for (int i = 0; i < NV; ++i) {
+    float v[E];
+    L::unpack(w[i], v);
+#pragma unroll
+    for (int e = 0; e < E; e += 2) l += exp2_fast((v[e] - m) * k) + exp2_fast((v[e + 1] - m) * k);
+  }
   return State{m, l};
 }
 
-__device__ __forceinline__ void normalise_chunk(const float* xb, float* yb, float m, float inv_l) {
-  f32x4 v[kChunkVec];
+template <typename T>
+__device__ __forceinline__ void normalise_chunk(const T* xb, T* yb, float m, float inv_l, float k) {
+  using L = Elem<T>;
+  constexpr int E = L::E, NV = (int)(kSoftmaxChunk / E / kThreads);
+  u32x4 w[NV];
 #pragma unroll
-  for (int i = 0; i < kChunkVec; ++i) v[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(xb) + threadIdx.x + i * kThreads);
+  for (int i = 0; i < NV; ++i)
+    w[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xb) + threadIdx.x + i * kThreads);
 #pragma unroll
-  for (int i = 0; i < kChunkVec; ++i) {
-    f32x4 r;
-    r.x = exp2_fast((v[i].x - m) * kLog2e) * inv_l;
-    r.y = exp2_fast((v[i].y - m) * kLog2e) * inv_l;
-    r.z = exp2_fast((v[i].z - m) * kLog2e) * inv_l;
-    r.w = exp2_fast((v[i].w - m) * kLog2e) * inv_l;
-    __builtin_nontemporal_store(r, reinterpret_cast<f32x4*>(yb) + threadIdx.x + i * kThreads);
+  for (int i = 0; i < NV; ++i) {
+    float v[E];
+    L::unpack(w[i], v);
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[e] = exp2_fast((v[e] - m) * k) * inv_l;
+    __builtin_nontemporal_store(L::pack(v), reinterpret_cast<u32x4*>(yb) + threadIdx.x + i * kThreads);
   }
 }
 
 // One workgroup per row: both passes.  x and y may be the same buffer.
-template <int VEC>
-__global__ __launch_bounds__(kThreads) void softmax_row_kernel(const float* x, float* y, int64_t cols) {
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kThreads) void softmax_row_kernel(const T* x, T* y, int64_t cols, float k,
+                                                               int64_t period) {
   __shared__ float sm[2 * kWaves];
   const int64_t row = blockIdx.x;
-  const float* xr = x + row * cols;
-  float* yr = y + row * cols;
-  State s = scan<VEC>(xr, 0, cols);
-  s = block_merge(s, sm);
-  normalise<VEC>(xr, yr, 0, cols, s.m, 1.0f / s.l);
+  const int64_t lim = row_limit(row, cols, period);
+  const T* xr = x + row * cols;
+  T* yr = y + row * cols;
+  State s = scan<T, VEC>(xr, 0, lim, k);
+  s = block_merge(s, sm, k);
+  normalise<T, VEC>(xr, yr, 0, lim, s.m, 1.0f / s.l, k);
+  zero_fill<T, VEC>(yr, lim, cols);
 }
 
-// Split rows, pass 1: the (m, l) partial of one chunk.
-template <int VEC>
-__global__ __launch_bounds__(kThreads) void softmax_split_pass1(const float* __restrict__ x, float* __restrict__ part,
-                                                                int64_t cols, int splits, int64_t chunk) {
+// Split rows, pass 1: the (m, l) partial of one chunk (empty when the chunk is
+// wholly masked).
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kThreads) void softmax_split_pass1(const T* __restrict__ x, float* __restrict__ part,
+                                                                int64_t cols, int splits, int64_t chunk, float k,
+                                                                int64_t period) {
   __shared__ float sm[2 * kWaves];
   const int64_t id = blockIdx.x;
   const int64_t row = id / splits;
   const int64_t ck = id - row * splits;
+  const int64_t lim = row_limit(row, cols, period);
   const int64_t begin = ck * chunk;
-  const int64_t end = begin + chunk < cols ? begin + chunk : cols;
-  State s = (VEC == 4 && end - begin == kSoftmaxChunk) ? scan_chunk(x + row * cols + begin)
-                                                        : scan<VEC>(x + row * cols, begin, end);
-  s = block_merge(s, sm);
+  int64_t end = begin + chunk < cols ? begin + chunk : cols;
+  if (end > lim) end = lim;
+  State s = (VEC && end - begin == kSoftmaxChunk) ? scan_chunk(x + row * cols + begin, k)
+                                                  : scan<T, VEC>(x + row * cols, begin, end, k);
+  s = block_merge(s, sm, k);
   if (threadIdx.x == 0) {
     part[2 * id] = s.m;
     part[2 * id + 1] = s.l;
@@ -199,53 +303,59 @@ __global__ __launch_bounds__(kThreads) void softmax_split_pass1(const float* __r
 }
 
 // Split rows, pass 2: merge the row's partials, then normalise one chunk.
-template <int VEC>
-__global__ __launch_bounds__(kThreads) void softmax_split_pass2(const float* x, float* y,
-                                                                const float* __restrict__ part, int64_t cols,
-                                                                int splits, int64_t chunk) {
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kThreads) void softmax_split_pass2(const T* x, T* y, const float* __restrict__ part,
+                                                                int64_t cols, int splits, int64_t chunk, float k,
+                                                                int64_t period) {
   __shared__ float sm[2 * kWaves];
   const int64_t id = blockIdx.x;
   const int64_t row = id / splits;
   const int64_t ck = id - row * splits;
   State s = {kNegInf, 0.f};
   const float* pr = part + 2 * row * splits;
-  for (int i = threadIdx.x; i < splits; i += kThreads) merge_state(s, pr[2 * i], pr[2 * i + 1]);
-  s = block_merge(s, sm);
+  for (int i = threadIdx.x; i < splits; i += kThreads) merge_state(s, pr[2 * i], pr[2 * i + 1], k);
+  s = block_merge(s, sm, k);
+  const int64_t lim = row_limit(row, cols, period);
   const int64_t begin = ck * chunk;
   const int64_t end = begin + chunk < cols ? begin + chunk : cols;
-  if (VEC == 4 && end - begin == kSoftmaxChunk)
-    normalise_chunk(x + row * cols + begin, y + row * cols + begin, s.m, 1.0f / s.l);
+  const int64_t vis = end < lim ? end : lim;
+  if (VEC && vis - begin == kSoftmaxChunk)
+    normalise_chunk(x + row * cols + begin, y + row * cols + begin, s.m, 1.0f / s.l, k);
   else
-    normalise<VEC>(x + row * cols, y + row * cols, begin, end, s.m, 1.0f / s.l);
+    normalise<T, VEC>(x + row * cols, y + row * cols, begin, vis, s.m, 1.0f / s.l, k);
+  zero_fill<T, VEC>(y + row * cols, vis > begin ? vis : begin, end);
 }
 
-}  // namespace
-
-hipError_t launch_softmax_rows(const SoftmaxArgs& a) {
-  const bool vec = (a.cols % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.x) & 15) == 0) &&
-                   ((reinterpret_cast<uintptr_t>(a.y) & 15) == 0);
+template <typename T, bool VEC>
+hipError_t launch_t(const SoftmaxArgs& a) {
+  const T* x = static_cast<const T*>(a.x);
+  T* y = static_cast<T*>(a.y);
   const dim3 block(kThreads);
   if (a.plan.kernel == OSX_KERNEL_SOFTMAX_ROW) {
-    const dim3 grid((unsigned)a.rows);
-    if (vec)
-      hipLaunchKernelGGL(softmax_row_kernel<4>, grid, block, 0, a.stream, a.x, a.y, a.cols);
-    else
-      hipLaunchKernelGGL(softmax_row_kernel<1>, grid, block, 0, a.stream, a.x, a.y, a.cols);
+    hipLaunchKernelGGL((softmax_row_kernel<T, VEC>), dim3((unsigned)a.rows), block, 0, a.stream, x, y, a.cols, a.k,
+                       a.period);
     return hipGetLastError();
   }
   float* part = static_cast<float*>(a.workspace);
   const dim3 grid((unsigned)a.plan.grid);
   const int64_t chunk = a.plan.block_m;
-  if (vec) {
-    hipLaunchKernelGGL(softmax_split_pass1<4>, grid, block, 0, a.stream, a.x, part, a.cols, a.plan.splits, chunk);
-    hipLaunchKernelGGL(softmax_split_pass2<4>, grid, block, 0, a.stream, a.x, a.y, part, a.cols, a.plan.splits,
-                       chunk);
-  } else {
-    hipLaunchKernelGGL(softmax_split_pass1<1>, grid, block, 0, a.stream, a.x, part, a.cols, a.plan.splits, chunk);
-    hipLaunchKernelGGL(softmax_split_pass2<1>, grid, block, 0, a.stream, a.x, a.y, part, a.cols, a.plan.splits,
-                       chunk);
-  }
+  hipLaunchKernelGGL((softmax_split_pass1<T, VEC>), grid, block, 0, a.stream, x, part, a.cols, a.plan.splits, chunk,
+                     a.k, a.period);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((softmax_split_pass2<T, VEC>), grid, block, 0, a.stream, x, y, part, a.cols, a.plan.splits,
+                     chunk, a.k, a.period);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_softmax_rows(const SoftmaxArgs& a) {
+  const int E = a.dtype == OSX_BF16 ? Elem<uint16_t>::E : Elem<float>::E;
+  const bool vec = (a.cols % E == 0) && ((reinterpret_cast<uintptr_t>(a.x) & 15) == 0) &&
+                   ((reinterpret_cast<uintptr_t>(a.y) & 15) == 0);
+  if (a.dtype == OSX_BF16) return vec ? launch_t<uint16_t, true>(a) : launch_t<uint16_t, false>(a);
+  return vec ? launch_t<float, true>(a) : launch_t<float, false>(a);
 }
 
 }  // namespace osx

@@ -75,3 +75,16 @@ def attention_lse(q, k, causal=False, scale=None):
             ob.append(oh)
         out.append(ob)
     return out
+
+
+def softmax_masked(rows, causal_period=0, scale=1.0):
+    """Row softmax of scale * x; with causal_period P, row r keeps columns c <= r mod P (others 0)."""
+    out = []
+    for r, row in enumerate(rows):
+        lim = len(row) if not causal_period else min(len(row), r % causal_period + 1)
+        vals = [float(v) * scale for v in row[:lim]]
+        mx = max(vals)
+        w = [math.exp(v - mx) for v in vals]
+        tot = math.fsum(w)
+        out.append([t / tot for t in w] + [0.0] * (len(row) - lim))
+    return out

@@ -11,6 +11,9 @@ BF16_ATOL, BF16_RTOL = 2e-2, 1e-2
 # the sum is taken over P rounded to bf16 (relative error <= 2^-9 each, so the
 # sum's relative error is below 2^-9 and ln of it below 2e-3) -> 4e-3 absolute.
 LSE_F32_ATOL, LSE_BF16_ATOL = 5e-5, 4e-3
+# Row softmax with bf16 output: y is rounded to bf16 (relative error <= 2^-9)
+# after fp32 arithmetic (relative ~1e-6): |err| <= 2^-8 |y*| + 1e-6.
+SOFTMAX_BF16_RTOL, SOFTMAX_BF16_ATOL = 2.0 ** -8, 1e-6
 
 
 def to_dev(a: np.ndarray, device="cuda"):

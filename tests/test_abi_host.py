@@ -129,3 +129,17 @@ def test_attn_fwd_lse_rejects_before_launch():
     assert st == osx.OSX_EINVAL and "overlap" in osx.last_error()
     # no work: OK without pointers
     assert lib.osx_attn_fwd_lse(None, None, None, None, None, BF16, 0, 4, 1, 16, 16, 128, 1, 0.0, None, 0, None) == 0
+
+
+def test_softmax_rows_ex_rejects_before_launch():
+    lib = osx.lib
+    x, y = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x900000)
+    assert lib.osx_softmax_rows_ex(x, y, 7, 4, 16, 0, 1.0, None, 0, None) == osx.OSX_EINVAL  # dtype
+    assert lib.osx_softmax_rows_ex(x, y, F32, 4, 16, -1, 1.0, None, 0, None) == osx.OSX_EINVAL  # period
+    assert lib.osx_softmax_rows_ex(x, y, F32, 4, 16, 0, 0.0, None, 0, None) == osx.OSX_EINVAL  # scale
+    assert lib.osx_softmax_rows_ex(x, y, F32, 4, 16, 0, float("inf"), None, 0, None) == osx.OSX_EINVAL
+    # bf16 elements are 2 bytes: a y 8 bytes after x overlaps 4x16 bf16 values
+    assert lib.osx_softmax_rows_ex(x, ctypes.c_void_p(0x100000 + 8), BF16, 4, 16, 0, 1.0, None, 0,
+                                   None) == osx.OSX_EINVAL
+    assert lib.osx_softmax_rows_ex(x, y, BF16, 1, 1 << 20, 0, 1.0, None, 0, None) == osx.OSX_EWORKSPACE
+    assert lib.osx_softmax_rows_ex(None, None, BF16, 0, 16, 3, 1.0, None, 0, None) == 0

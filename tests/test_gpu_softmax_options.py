@@ -1,0 +1,109 @@
+"""GPU parity of osx_softmax_rows_ex (scale, causal mask, bf16 in/out) against the fp64 oracle.
+
+Covers the one-workgroup-per-row kernel and the split (chunked) kernels,
+16-byte and scalar paths (column counts that are and are not multiples of the
+vector width), chunks that are wholly, partly or not masked, and in place.
+Masked outputs must be exactly 0.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import F32_ATOL, SOFTMAX_BF16_ATOL, SOFTMAX_BF16_RTOL, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+CASES = [  # dtype, rows, cols, causal_period, scale
+    ("f32", 64, 100, 64, 0.125),       # one causal [64, 100] score matrix
+    ("f32", 4096, 4096, 4096, 0.0883883),  # a full causal 4096 x 4096 head, row kernel
+    ("bf16", 150, 77, 50, 1.0),        # three heads of [50, 77], scalar path (77 % 8 != 0)
+    ("f32", 140, 101, 70, 0.3),        # two heads of [70, 101], scalar path (101 % 4 != 0)
+    ("bf16", 96, 4096, 48, 0.5),       # vector path, period < cols
+    ("bf16", 2, 65536, 0, 2.0),        # split, 16-byte path, full chunks
+    ("bf16", 2, 100003, 0, 1.0),       # split, scalar path, ragged last chunk
+    ("f32", 3, 40000, 3, 1.0),         # split: all but the first chunk wholly masked
+    ("f32", 2, 20000, 0, 0.75),        # split, scale only
+]
+
+
+@pytest.fixture(scope="module")
+def osx():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import online_softmax_02_amd
+    return online_softmax_02_amd
+
+
+def _inputs(dtype, rows, cols, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.normal(0.0, 3.0, (rows, cols)).astype(np.float32)
+    return synth.round_to_bf16_bits(x) if dtype == "bf16" else x
+
+
+def _check(got, ref, dtype, period, what):
+    rows, cols = ref.shape
+    assert np.isfinite(got).all(), what
+    if period:
+        lim = np.minimum(np.arange(rows) % period + 1, cols)
+        masked = np.arange(cols)[None, :] >= lim[:, None]
+        assert (got[masked] == 0).all(), f"{what}: masked outputs are not 0"
+    err = np.abs(got - ref)
+    if dtype == "f32":
+        assert err.max() <= F32_ATOL, f"{what}: max abs error {err.max():.3e}"
+    else:
+        bad = err > SOFTMAX_BF16_ATOL + SOFTMAX_BF16_RTOL * np.abs(ref)
+        assert not bad.any(), f"{what}: {int(bad.sum())} outputs off, worst {err.max():.3e}"
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
+def test_softmax_options_match_oracle(osx, case):
+    dtype, rows, cols, period, scale = case
+    if rows * cols > (1 << 26):  # keep the fp64 oracle within a few seconds: check a band of rows
+        pytest.skip("too large for the element-wise check")
+    print(f"case softmax_ex {case}", flush=True)
+    x = _inputs(dtype, rows, cols, rows + cols)
+    y = osx.softmax_rows(to_dev(x), causal_period=period, scale=scale)
+    torch.cuda.synchronize()
+    _check(to_f64(y), oracle.softmax_rows(x, causal_period=period, scale=scale), dtype, period, str(case))
+
+
+def test_softmax_options_large_masked_rows_sampled(osx):
+    """[16400, 16500] fp32, one causal head: rows are split into 2 chunks and their visible part ends in
+    chunk 0, exactly at the chunk edge, or in chunk 1; sampled rows against the oracle."""
+    rows, cols = 16400, 16500
+    x = _inputs("f32", rows, cols, 11)
+    y = osx.softmax_rows(to_dev(x), causal_period=rows)
+    torch.cuda.synchronize()
+    pick = np.array([0, 1, 5000, 16382, 16383, 16384, 16385, 16399])
+    got = y[torch.from_numpy(pick).cuda()].cpu().numpy().astype(np.float64)
+    ref = np.stack([oracle.softmax_rows(x[pick[i]:pick[i] + 1], scale=1.0)[0] * 0 for i in range(len(pick))])
+    for i, r in enumerate(pick):  # row r keeps columns <= r: the oracle on that row's visible prefix
+        ref[i, :r + 1] = oracle.softmax_rows(x[r:r + 1, :r + 1])[0]
+    _check(got, ref, "f32", 0, "sampled rows")
+    for i, r in enumerate(pick):
+        assert (got[i, r + 1:] == 0).all()
+
+
+def test_softmax_options_in_place_bf16(osx):
+    x = _inputs("bf16", 40, 4096, 5)
+    xd = to_dev(x)
+    y = osx.softmax_rows(xd, out=xd, causal_period=40, scale=0.25)
+    torch.cuda.synchronize()
+    assert y.data_ptr() == xd.data_ptr()
+    _check(to_f64(y), oracle.softmax_rows(x, causal_period=40, scale=0.25), "bf16", 40, "in place")
+
+
+def test_softmax_options_defaults_equal_plain_softmax(osx):
+    """scale 1 and no mask through osx_softmax_rows_ex give the same bits as osx_softmax_rows."""
+    x = to_dev(_inputs("f32", 3, 30000, 9))
+    plain = osx.softmax_rows(x)
+    ex = torch.empty_like(x)
+    st = osx.lib.osx_softmax_rows_ex(x.data_ptr(), ex.data_ptr(), osx.OSX_F32, 3, 30000, 0, 1.0,
+                                     torch.empty(osx.softmax_rows_workspace(3, 30000), dtype=torch.uint8,
+                                                 device="cuda").data_ptr(), osx.softmax_rows_workspace(3, 30000),
+                                     torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == 0
+    assert torch.equal(plain, ex)

@@ -300,3 +300,39 @@ def test_lse_is_the_recurrence_final_state():
     for i, hist in enumerate(traces):
         m, l, _ = hist[-1]
         assert abs(m + math.log(l) - lse[i]) < 1e-12
+
+
+# ---------------------------------------------------------------- softmax options
+def test_softmax_causal_constant_rows_are_uniform_over_visible_columns():
+    """Constant logits: row r of each [P, cols] matrix is 1/(r mod P + 1) on columns <= r mod P, 0 after."""
+    P, cols = 5, 7
+    y = oracle.softmax_rows(np.full((2 * P, cols), 3.25), causal_period=P)
+    for r in range(2 * P):
+        lim = min(cols, r % P + 1)
+        np.testing.assert_allclose(y[r, :lim], 1.0 / lim, rtol=1e-15)
+        assert (y[r, lim:] == 0).all()
+
+
+def test_softmax_scale_two_elements_is_logistic():
+    """softmax(scale * [a, b])[0] = 1 / (1 + e^{scale (b - a)})."""
+    for a, b, sc in [(3.0, -1.0, 0.125), (-7.5, 2.25, 2.0)]:
+        y = oracle.softmax_rows(np.array([[a, b]]), scale=sc)[0]
+        assert y[0] == pytest.approx(1.0 / (1.0 + math.exp(sc * (b - a))), rel=1e-15)
+
+
+def test_softmax_masked_matches_library_on_the_visible_prefix():
+    x = RNG.normal(0, 3, (12, 9))
+    y = oracle.softmax_rows(x, causal_period=6, scale=0.5)
+    for r in range(12):
+        lim = r % 6 + 1
+        np.testing.assert_allclose(y[r, :lim], scipy.special.softmax(0.5 * x[r, :lim]), rtol=1e-13)
+        np.testing.assert_allclose(y[r].sum(), 1.0, rtol=1e-13)
+
+
+def test_softmax_masked_brute_force_and_bf16_decoding():
+    x = RNG.normal(0, 2, (7, 5))
+    np.testing.assert_allclose(oracle.softmax_rows(x, causal_period=3, scale=1.5),
+                               brute.softmax_masked(x.tolist(), 3, 1.5), rtol=1e-13, atol=1e-300)
+    bits = np.array([[0x3F80, 0x4000, 0xC040]], dtype=np.uint16)  # 1, 2, -3 in bf16
+    np.testing.assert_allclose(oracle.softmax_rows(bits), oracle.softmax_rows(np.array([[1.0, 2.0, -3.0]])),
+                               rtol=1e-15)
