@@ -6,8 +6,9 @@ B=2, Hq=32, Hkv=8, S=4096, d=128): every step of the single-pass attention
 hot path runs in it.  The headline ``value`` is its causal-adjusted TFLOP/s
 (4*B*Hq*S*S*d / 2 flops per call).  The other hot-path calls are timed in the
 same run and reported under ``also``: GQA decode (GB/s over K/V), the long-row
-softmax (GB/s, 2 reads + 1 write), the fp32 4096^2 attention (TFLOP/s) and the
-two small latency cases (microseconds).
+softmax and the causal bf16 score-row softmax (GB/s: the visible inputs read
+twice, or once where the row stays in registers, + 1 write), the fp32 4096^2
+attention (TFLOP/s) and the two small latency cases (microseconds).
 
 Inputs are seeded synthetic tensors (``synth``), generated on the host and
 copied to HBM before timing.  Durations come from one HIP event pair recorded
@@ -36,6 +37,7 @@ KERNEL_SOURCES = {
     "prefill_bf16_kernel": "online_softmax_02_amd/csrc/attn_prefill_bf16.hip",
     "decode_bf16_kernel": "online_softmax_02_amd/csrc/attn_decode_bf16.hip",
     "softmax_split": "online_softmax_02_amd/csrc/softmax_rows.hip",
+    "softmax_wave_causal": "online_softmax_02_amd/csrc/softmax_rows.hip",
     "prefill_f32_kernel": "online_softmax_02_amd/csrc/attn_prefill_f32.hip",
 }
 
@@ -151,6 +153,11 @@ def bench_decode(torch, osx, args):
             "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", traffic_for("decode_bf16_kernel"))}
 
 
+def softmax_reads(osx, w):
+    """Times the planned kernels read x from memory: once when a row stays in registers, twice when split."""
+    return 2 if osx.softmax_rows_plan(w.rows, w.cols)["kernel_name"] == "softmax_split" else 1
+
+
 def bench_softmax(torch, osx, args):
     import synth
     w = synth.WORKLOADS["softmax_1x16m"]
@@ -161,10 +168,30 @@ def bench_softmax(torch, osx, args):
     ws = torch.empty(osx.softmax_rows_workspace(w.rows, w.cols), dtype=torch.uint8, device="cuda")
     wall, ms = timed(torch, lambda i: osx.softmax_rows(xs[i % 5], out=ys[i % 5], workspace=ws), args.steps,
                      args.warmup)
-    gbs = w.bytes() / (ms * 1e-3) / 1e9
+    reads = softmax_reads(osx, w)
+    gbs = w.bytes(reads) / (ms * 1e-3) / 1e9
     return {"workload": w.name, "unit": "GB/s", "value": round(gbs, 1), "call_us": round(ms * 1e3, 2),
-            "bytes_per_call": w.bytes(),
+            "bytes_per_call": w.bytes(reads), "reads_of_x": reads,
             "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", traffic_for("softmax_split"))}
+
+
+def bench_softmax_causal(torch, osx, args):
+    """Causal bf16 score rows: one workgroup per row reads the visible columns and zero-fills the rest."""
+    import synth
+    w = synth.WORKLOADS["softmax_causal_bf16"]
+    x = to_dev(synth.softmax_inputs(w))
+    # 5 input/output pairs (1.3 GB) rotate so no call finds its data in the 256 MB MALL.
+    xs = [x.clone() for _ in range(5)]
+    ys = [torch.empty_like(x) for _ in range(5)]
+    ws = torch.empty(max(1, osx.softmax_rows_workspace(w.rows, w.cols)), dtype=torch.uint8, device="cuda")
+    wall, ms = timed(torch, lambda i: osx.softmax_rows(xs[i % 5], out=ys[i % 5], workspace=ws,
+                                                       causal_period=w.causal_period, scale=w.scale),
+                     args.steps, args.warmup)
+    reads = softmax_reads(osx, w)
+    gbs = w.bytes(reads) / (ms * 1e-3) / 1e9
+    return {"workload": w.name, "unit": "GB/s", "value": round(gbs, 1), "call_us": round(ms * 1e3, 2),
+            "bytes_per_call": w.bytes(reads), "reads_of_x": reads,
+            "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", traffic_for("softmax_wave_causal"))}
 
 
 def bench_f32(torch, osx, args):
@@ -251,6 +278,7 @@ def main():
         return
     if args.only in ("softmax",):
         also["softmax_1x16m"] = bench_softmax(torch, osx, args)
+        also["softmax_causal_bf16"] = bench_softmax_causal(torch, osx, args)
         print(json.dumps({"also": also}))
         return
     if args.only in ("f32",):
@@ -268,6 +296,8 @@ def main():
         log(f"[bench] decode {also['gqa_decode_bf16']['value']} GB/s")
         also["softmax_1x16m"] = bench_softmax(torch, osx, args)
         log(f"[bench] softmax {also['softmax_1x16m']['value']} GB/s")
+        also["softmax_causal_bf16"] = bench_softmax_causal(torch, osx, args)
+        log(f"[bench] causal bf16 softmax {also['softmax_causal_bf16']['value']} GB/s")
         also["attn_f32_4k_d128"] = bench_f32(torch, osx, args)
         log(f"[bench] fp32 attention {also['attn_f32_4k_d128']['value']} TFLOP/s")
         also.update(bench_small(torch, osx, args))

@@ -53,8 +53,9 @@ extern "C" {
 #define OSX_KERNEL_PREFILL_F32 1   /* fp32 MFMA tiles, any seq_q */
 #define OSX_KERNEL_PREFILL_BF16 2  /* bf16 MFMA tiles, any seq_q */
 #define OSX_KERNEL_DECODE_BF16 3   /* bf16, seq_q == 1: K/V split across workgroups + combine */
-#define OSX_KERNEL_SOFTMAX_ROW 4   /* one workgroup per row */
+#define OSX_KERNEL_SOFTMAX_ROW 4   /* one workgroup per row, the row held in registers */
 #define OSX_KERNEL_SOFTMAX_SPLIT 5 /* rows split across workgroups, (m, l) partials merged */
+#define OSX_KERNEL_SOFTMAX_WAVE 6  /* one wavefront per row, the row held in registers */
 
 /* What the library will launch for a given problem (filled by the plan calls). */
 typedef struct osx_plan {
@@ -124,14 +125,16 @@ int osx_attn_fwd_lse(const void* q, const void* k, const void* v, void* o, float
 /* osx_softmax_rows_plan -- kernel choice for x[rows, cols]; no HIP calls. */
 int osx_softmax_rows_plan(int64_t rows, int64_t cols, osx_plan* out);
 
-/* Workspace bytes osx_softmax_rows needs for x[rows, cols] (0 when one workgroup per row), via *bytes. */
+/* Workspace bytes osx_softmax_rows needs for x[rows, cols] (0 unless rows are split), via *bytes. */
 int osx_softmax_rows_workspace(int64_t rows, int64_t cols, size_t* bytes);
 
 /*
  * osx_softmax_rows -- y[r, :] = exp(x[r, :] - m_r) / l_r for every row r, with
  * m_r the row max and l_r = sum_j exp(x[r, j] - m_r), found in one online pass
  * over x, then a second pass over x writes y (page "Softmax 算子的实现与优化",
- * section Online Softmax).
+ * section Online Softmax).  Rows of up to 8192 columns are held on chip
+ * between the passes, so x is read from memory once; longer rows are read
+ * twice.
  *
  * x, y: device fp32 [rows, cols], contiguous.  y == x (in place) is allowed;
  * any other overlap is OSX_EINVAL.  cols == 0 with rows > 0 is OSX_EINVAL (a
@@ -151,7 +154,8 @@ int osx_softmax_rows(const float* x, float* y, int64_t rows, int64_t cols, void*
  * c <= r mod P (x is a stack of [P, cols] score matrices, one per head, and
  * the mask is page "从零开始写Qwen3（五-其一）使用Triton实现自注意力", section
  * softmax的triton实现: column <= row, the rest loaded as -inf).  Every row
- * keeps column 0.  Masked columns of x are not read.
+ * keeps column 0.  Masked columns of x beyond the 16-byte vector holding a
+ * row's last visible column are not read.
  * scale: positive and finite (1 for none); it multiplies x before the
  * softmax (the attention scale d^-1/2 of page "softmax_attention").
  * workspace: as for osx_softmax_rows (osx_softmax_rows_workspace gives the

@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(_HERE, "libosx.so")
 
 OSX_OK, OSX_EINVAL, OSX_EUNSUPPORTED, OSX_EHIP, OSX_EWORKSPACE = 0, -1, -2, -3, -4
 OSX_F32, OSX_BF16 = 0, 1
-KERNELS = {0: "none", 1: "prefill_f32", 2: "prefill_bf16", 3: "decode_bf16", 4: "softmax_row", 5: "softmax_split"}
+KERNELS = {0: "none", 1: "prefill_f32", 2: "prefill_bf16", 3: "decode_bf16", 4: "softmax_row", 5: "softmax_split",
+           6: "softmax_wave"}
 
 _i, _i64, _sz, _vp, _f = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
 

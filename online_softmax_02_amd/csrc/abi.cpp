@@ -105,7 +105,13 @@ int plan_softmax(int64_t rows, int64_t cols, osx_plan* p) {
   if (rows == 0) return ok();
   if (cols == 0) return fail(OSX_EINVAL, "cols == 0 with rows > 0: softmax over nothing");
   p->threads = osx::kSoftmaxThreads;
-  if (cols <= osx::kSoftmaxRowMax) {
+  if (cols <= osx::kSoftmaxWaveMax) {
+    p->kernel = OSX_KERNEL_SOFTMAX_WAVE;
+    p->block_m = (int)cols;
+    p->splits = 1;
+    p->grid = cdiv(rows, osx::kSoftmaxThreads / osx::kWaveSize);
+    p->workspace_bytes = 0;
+  } else if (cols <= osx::kSoftmaxRowMax) {
     p->kernel = OSX_KERNEL_SOFTMAX_ROW;
     p->block_m = (int)cols;
     p->splits = 1;

@@ -24,7 +24,8 @@ constexpr int kDecodeTargetWgs = 4096;
 constexpr int kSplitTargetWgs = 512;   // fp32 prefill: split the keys below this many workgroups
 constexpr int kSplitMinBlocks = 4;     // ... keeping at least this many key blocks per slice
 constexpr int kSoftmaxThreads = 256;
-constexpr int64_t kSoftmaxRowMax = 8192;   // longest row handled by one workgroup
+constexpr int64_t kSoftmaxWaveMax = 2048;  // longest row held by one wavefront (32 elements per lane)
+constexpr int64_t kSoftmaxRowMax = 8192;   // longest row held by one workgroup (32 elements per thread)
 constexpr int64_t kSoftmaxChunk = 16384;   // elements per workgroup when a row is split
 
 struct AttnArgs {

@@ -15,13 +15,17 @@
 // stacked [P, cols] score matrices of several heads.  Masked columns are never
 // read; they are written as 0.
 //
-// Two shapes of launch:
-//  * rows up to kSoftmaxRowMax elements: one workgroup per row does both
-//    passes (the pages keep (m, l) inside one program for consistency);
+// Three shapes of launch, by row length:
+//  * rows up to kSoftmaxWaveMax elements: one wavefront per row, the row held
+//    in its registers, so x is read from memory once; the per-lane states merge
+//    by lane shuffles, with no barrier;
+//  * rows up to kSoftmaxRowMax elements: the same with one workgroup per row,
+//    merged through LDS (the pages keep (m, l) inside one program);
 //  * longer rows: the row is cut into kSoftmaxChunk-element chunks, one
 //    workgroup each.  Pass 1 writes one (m, l) partial per chunk; pass 2 merges
-//    a row's partials with the same rescaling rule, then normalises its chunk.
-//    This replaces the single-program scan, which cannot use more than one CU.
+//    a row's partials with the same rescaling rule, then reads its chunk again
+//    and normalises it.  This replaces the single-program scan, which cannot
+//    use more than one CU.
 //
 // Exponentials are 2^((x - m) * k) with k = scale * log2 e, on the
 // transcendental unit.
@@ -108,14 +112,20 @@ __device__ __forceinline__ void update(State& s, const float (&v)[N], float k) {
   s.m = mn;
 }
 
-// Merge the states of all threads of the workgroup; every thread gets the result.
-__device__ __forceinline__ State block_merge(State s, float* sm /* 2*kWaves floats */, float k) {
+// Merge the states of the 64 lanes of a wavefront; every lane gets the result.
+__device__ __forceinline__ State wave_merge(State s, float k) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     const float mb = __shfl_xor(s.m, o, 64);
     const float lb = __shfl_xor(s.l, o, 64);
     merge_state(s, mb, lb, k);
   }
+  return s;
+}
+
+// Merge the states of all threads of the workgroup; every thread gets the result.
+__device__ __forceinline__ State block_merge(State s, float* sm /* 2*kWaves floats */, float k) {
+  s = wave_merge(s, k);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) {
     sm[2 * wave] = s.m;
@@ -264,19 +274,143 @@ __device__ __forceinline__ void normalise_chunk(const T* xb, T* yb, float m, flo
   }
 }
 
-// One workgroup per row: both passes.  x and y may be the same buffer.
-template <typename T, bool VEC>
+// A row held in registers: R threads (one wavefront, or the whole workgroup)
+// cover one row, thread t holding the 16-byte vectors t, t + R, ... (VEC) or
+// the elements t, t + R, ... (scalar), NV vectors' worth either way.  Each
+// thread folds its visible values into (m, l); the states merge across the R
+// threads; the outputs come from the registers, so x is read once.  x and y
+// may be the same buffer: a row's reads all feed the merge, which comes before
+// its first store of a visible column, and its early stores (the masked
+// vectors) never overlap the vectors it reads.
+
+constexpr int kNonTemporal = 2;               // buffer-op cache policy: x and y are streamed once
+constexpr uint32_t kOffNowhere = 0x80000000u;  // a buffer offset past any row: the store is dropped
+
+// 16-byte path, first half of a row: load the nvis vectors that hold a visible
+// column (the buffer returns 0 past them) and store 0 to the masked vectors
+// (nvis <= vi < nv), which do not depend on x, while the loads are in flight.
+// The accesses are unconditional buffer operations, so the loads issue back to
+// back and the compiler's wait counts are exact.
+template <typename T, int NV, int R>
+__device__ __forceinline__ void vec_issue(const T* xr, T* yr, uint32_t nvis, uint32_t nv, int t, u32x4 (&w)[NV]) {
+  const __amdgpu_buffer_rsrc_t xs = make_rsrc(xr, nvis * 16u);
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    w[i] = __builtin_amdgcn_raw_buffer_load_b128(xs, 16u * (uint32_t)(t + R * i), 0, kNonTemporal);
+  const __amdgpu_buffer_rsrc_t zs = make_rsrc(yr, nv * 16u);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const uint32_t vi = (uint32_t)(t + R * i);
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, zs, vi >= nvis ? 16u * vi : kOffNowhere, 0,
+                                           kNonTemporal);
+  }
+}
+
+// Second half: (m, l) of the visible values (column < lim), merged over the
+// R threads; then y = 2^((x - m) k) / l for the nvis loaded vectors (0 for
+// their masked columns).
+template <typename T, int NV, int R>
+__device__ __forceinline__ void vec_finish(T* yr, int lim, uint32_t nvis, int t, const u32x4 (&w)[NV], float k,
+                                           float* sm) {
+  using L = Elem<T>;
+  constexpr int E = L::E, N = NV * E;
+  float v[N];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    float f[E];
+    L::unpack(w[i], f);
+    const int c0 = E * (t + R * i);  // resident rows have at most kSoftmaxRowMax columns
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[i * E + e] = c0 + e < lim ? f[e] : kNegInf;
+  }
+  float m = v[0];
+#pragma unroll
+  for (int j = 1; j < N; ++j) m = fmaxf(m, v[j]);
+  float l = 0.f;
+  if (m != kNegInf) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) l += exp2_fast((v[j] - m) * k);  // -inf -> 0
+  }
+  State s = {m, l};
+  s = R == kWaveSize ? wave_merge(s, k) : block_merge(s, sm, k);
+  const float inv_l = 1.0f / s.l;
+  const __amdgpu_buffer_rsrc_t ys = make_rsrc(yr, nvis * 16u);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    float f[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) f[e] = exp2_fast((v[i * E + e] - s.m) * k) * inv_l;
+    __builtin_amdgcn_raw_buffer_store_b128(L::pack(f), ys, 16u * (uint32_t)(t + R * i), 0, kNonTemporal);
+  }
+}
+
+// Scalar path (cols not a multiple of the vector width, or x / y not 16-byte
+// aligned): one row, elements t, t + R, ...
+template <typename T, int NV, int R>
+__device__ __forceinline__ void scalar_row(const T* xr, T* yr, int64_t lim, int64_t cols, int t, float k, float* sm) {
+  using L = Elem<T>;
+  constexpr int N = NV * L::E;
+  float v[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    const int64_t c = t + (int64_t)R * j;
+    v[j] = c < lim ? L::get(xr + c) : kNegInf;
+  }
+  float m = v[0];
+#pragma unroll
+  for (int j = 1; j < N; ++j) m = fmaxf(m, v[j]);
+  float l = 0.f;
+  if (m != kNegInf) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) l += exp2_fast((v[j] - m) * k);
+  }
+  State s = {m, l};
+  s = R == kWaveSize ? wave_merge(s, k) : block_merge(s, sm, k);
+  const float inv_l = 1.0f / s.l;
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    const int64_t c = t + (int64_t)R * j;
+    if (c >= cols) break;
+    L::put(yr + c, exp2_fast((v[j] - s.m) * k) * inv_l);  // 0 where masked (x = -inf)
+  }
+}
+
+// One wavefront per row, four rows per workgroup.
+template <typename T, bool VEC, int NV>
+__global__ __launch_bounds__(kThreads) void softmax_wave_kernel(const T* x, T* y, int64_t rows, int64_t cols, float k,
+                                                                int64_t period) {
+  constexpr int E = Elem<T>::E;
+  const int t = (int)threadIdx.x & (kWaveSize - 1);
+  const int64_t row = (int64_t)blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWaveSize);
+  if (row >= rows) return;  // a whole wavefront; no barrier follows
+  const int lim = (int)row_limit(row, cols, period);  // resident rows have at most kSoftmaxRowMax columns
+  if (VEC) {
+    const uint32_t nvis = __builtin_amdgcn_readfirstlane((uint32_t)((lim + E - 1) / E));
+    u32x4 w[NV];
+    vec_issue<T, NV, kWaveSize>(x + row * cols, y + row * cols, nvis, (uint32_t)(cols / E), t, w);
+    vec_finish<T, NV, kWaveSize>(y + row * cols, lim, nvis, t, w, k, nullptr);
+  } else {
+    scalar_row<T, NV, kWaveSize>(x + row * cols, y + row * cols, lim, cols, t, k, nullptr);
+  }
+}
+
+// One workgroup per row.
+template <typename T, bool VEC, int NV>
 __global__ __launch_bounds__(kThreads) void softmax_row_kernel(const T* x, T* y, int64_t cols, float k,
                                                                int64_t period) {
+  constexpr int E = Elem<T>::E;
   __shared__ float sm[2 * kWaves];
   const int64_t row = blockIdx.x;
   const int64_t lim = row_limit(row, cols, period);
-  const T* xr = x + row * cols;
-  T* yr = y + row * cols;
-  State s = scan<T, VEC>(xr, 0, lim, k);
-  s = block_merge(s, sm, k);
-  normalise<T, VEC>(xr, yr, 0, lim, s.m, 1.0f / s.l, k);
-  zero_fill<T, VEC>(yr, lim, cols);
+  const int t = (int)threadIdx.x;
+  if (VEC) {
+    const uint32_t nvis = __builtin_amdgcn_readfirstlane((uint32_t)((lim + E - 1) / E));
+    u32x4 w[NV];
+    vec_issue<T, NV, kThreads>(x + row * cols, y + row * cols, nvis, (uint32_t)(cols / E), t, w);
+    vec_finish<T, NV, kThreads>(y + row * cols, (int)lim, nvis, t, w, k, sm);
+  } else {
+    scalar_row<T, NV, kThreads>(x + row * cols, y + row * cols, lim, cols, t, k, sm);
+  }
 }
 
 // Split rows, pass 1: the (m, l) partial of one chunk (empty when the chunk is
@@ -326,16 +460,59 @@ __global__ __launch_bounds__(kThreads) void softmax_split_pass2(const T* x, T* y
   zero_fill<T, VEC>(y + row * cols, vis > begin ? vis : begin, end);
 }
 
+// Vectors per thread for a row held by R threads: cols / (R E), rounded up to
+// a power of two (at most 8: the planner keeps rows within 32 elements per thread).
+template <typename T>
+int vectors_per_thread(int64_t cols, int R) {
+  const int64_t per = (cols + (int64_t)R * Elem<T>::E - 1) / ((int64_t)R * Elem<T>::E);
+  return per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : per <= 8 ? 8 : 0;
+}
+
+template <typename T, bool VEC, int NV>
+hipError_t launch_wave_nv(const SoftmaxArgs& a, const T* x, T* y) {
+  if constexpr (NV * Elem<T>::E > 32) return hipErrorInvalidValue;  // never planned: at most 32 elements per lane
+  hipLaunchKernelGGL((softmax_wave_kernel<T, VEC, NV>), dim3((unsigned)a.plan.grid), dim3(kThreads), 0, a.stream, x, y,
+                     a.rows, a.cols, a.k, a.period);
+  return hipGetLastError();
+}
+
+template <typename T, bool VEC, int NV>
+hipError_t launch_row_nv(const SoftmaxArgs& a, const T* x, T* y) {
+  if constexpr (NV * Elem<T>::E > 32) return hipErrorInvalidValue;  // never planned: at most 32 elements per thread
+  hipLaunchKernelGGL((softmax_row_kernel<T, VEC, NV>), dim3((unsigned)a.plan.grid), dim3(kThreads), 0, a.stream, x, y,
+                     a.cols, a.k, a.period);
+  return hipGetLastError();
+}
+
+template <typename T, bool VEC>
+hipError_t launch_resident(const SoftmaxArgs& a) {
+  const T* x = static_cast<const T*>(a.x);
+  T* y = static_cast<T*>(a.y);
+  if (a.plan.kernel == OSX_KERNEL_SOFTMAX_WAVE) {
+    switch (vectors_per_thread<T>(a.cols, kWaveSize)) {
+      case 1: return launch_wave_nv<T, VEC, 1>(a, x, y);
+      case 2: return launch_wave_nv<T, VEC, 2>(a, x, y);
+      case 4: return launch_wave_nv<T, VEC, 4>(a, x, y);
+      case 8: return launch_wave_nv<T, VEC, 8>(a, x, y);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  switch (vectors_per_thread<T>(a.cols, kThreads)) {
+    case 1: return launch_row_nv<T, VEC, 1>(a, x, y);
+    case 2: return launch_row_nv<T, VEC, 2>(a, x, y);
+    case 4: return launch_row_nv<T, VEC, 4>(a, x, y);
+    case 8: return launch_row_nv<T, VEC, 8>(a, x, y);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <typename T, bool VEC>
 hipError_t launch_t(const SoftmaxArgs& a) {
   const T* x = static_cast<const T*>(a.x);
   T* y = static_cast<T*>(a.y);
   const dim3 block(kThreads);
-  if (a.plan.kernel == OSX_KERNEL_SOFTMAX_ROW) {
-    hipLaunchKernelGGL((softmax_row_kernel<T, VEC>), dim3((unsigned)a.rows), block, 0, a.stream, x, y, a.cols, a.k,
-                       a.period);
-    return hipGetLastError();
-  }
+  if (a.plan.kernel == OSX_KERNEL_SOFTMAX_WAVE || a.plan.kernel == OSX_KERNEL_SOFTMAX_ROW)
+    return launch_resident<T, VEC>(a);
   float* part = static_cast<float*>(a.workspace);
   const dim3 grid((unsigned)a.plan.grid);
   const int64_t chunk = a.plan.block_m;

@@ -79,10 +79,22 @@ class SoftmaxWorkload:
     sigma: float = 1.0
     spike: float | None = None  # value set at one index in the final 1% of each row
     kind: str = "softmax"
+    dtype: str = "f32"      # "f32" or "bf16" (input and output)
+    causal_period: int = 0  # > 0: row r keeps columns c <= r mod period
+    scale: float = 1.0      # logits are scale * x
 
-    def bytes(self) -> float:
-        """Algorithmic bytes: x read twice (two passes), y written once."""
-        return 3.0 * 4 * self.rows * self.cols
+    def visible(self) -> int:
+        """Number of unmasked elements over all rows."""
+        if self.causal_period <= 0:
+            return self.rows * self.cols
+        r = np.arange(self.rows, dtype=np.int64) % self.causal_period
+        return int(np.minimum(r + 1, self.cols).sum())
+
+    def bytes(self, reads: int = 2) -> float:
+        """Algorithmic bytes: the visible x read ``reads`` times (2 when the two passes each read it from memory,
+        1 when the row stays on chip between them), all of y written once."""
+        es = 2 if self.dtype == "bf16" else 4
+        return float(es * (reads * self.visible() + self.rows * self.cols))
 
 
 WORKLOADS = {
@@ -92,6 +104,9 @@ WORKLOADS = {
     "softmax_4x200": SoftmaxWorkload("softmax_4x200", 4, 200, seed=2, dist="uniform", low=-10.0, high=10.0),
     # Row softmax, one row of 2^24 ~ N(0, variance 4) with a +50 spike in the last 1%.
     "softmax_1x16m": SoftmaxWorkload("softmax_1x16m", 1, 1 << 24, seed=3, dist="normal", sigma=2.0, spike=50.0),
+    # Causal score rows in bf16: 16 heads of [2048, 2048] logits ~ N(0, 4), scale 1/sqrt(128).
+    "softmax_causal_bf16": SoftmaxWorkload("softmax_causal_bf16", 16 * 2048, 2048, seed=7, dist="normal", sigma=2.0,
+                                           dtype="bf16", causal_period=2048, scale=0.08838834764831845),
     # Single-head fp32 4096x4096, d=128; key row 3900 scaled by 8.
     "attn_f32_4k_d128": AttnWorkload("attn_f32_4k_d128", "f32", 1, 1, 1, 4096, 4096, 128, False, seed=4,
                                      planted_key=3900, planted_scale=8.0),
@@ -165,7 +180,7 @@ def attn_inputs(w: AttnWorkload, workers: int | None = None) -> dict:
 
 
 def softmax_inputs(w: SoftmaxWorkload) -> np.ndarray:
-    """x[rows, cols] fp32 for a softmax workload.
+    """x[rows, cols] for a softmax workload: fp32, or bf16 bit patterns (uint16).
 
     ``normal``: N(0, sigma^2) rows; with ``spike``, element ``cols-1-r`` of each
     row is set to the spike value, ``r`` uniform in [0, cols/100) (a late max).
@@ -181,6 +196,8 @@ def softmax_inputs(w: SoftmaxWorkload) -> np.ndarray:
         for r in range(w.rows):
             idx = w.cols - 1 - int(rng.integers(0, tail))
             x[r, idx] = np.float32(w.spike)
+    if w.dtype == "bf16":
+        return round_to_bf16_bits(x)
     return x
 
 

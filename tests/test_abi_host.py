@@ -104,8 +104,14 @@ def test_plans_for_the_workloads():
     assert p["workspace_bytes"] == 4096 * 16 * (2 + 128) * 4
     p = osx.attn_plan(BF16, 1, 40, 2, 1, 300, 128)  # 20 query heads per KV head: too many to pack
     assert p["kernel_name"] == "prefill_bf16"
-    p = osx.softmax_rows_plan(4, 200)
-    assert p["kernel_name"] == "softmax_row" and p["workspace_bytes"] == 0
+    p = osx.softmax_rows_plan(4, 200)  # one wavefront per row, four rows per workgroup
+    assert p["kernel_name"] == "softmax_wave" and p["workspace_bytes"] == 0 and p["grid"] == 1
+    p = osx.softmax_rows_plan(32768, 2048)
+    assert p["kernel_name"] == "softmax_wave" and p["grid"] == 8192
+    p = osx.softmax_rows_plan(4096, 2049)  # one workgroup per row
+    assert p["kernel_name"] == "softmax_row" and p["grid"] == 4096 and p["workspace_bytes"] == 0
+    assert osx.softmax_rows_plan(3, 8192)["kernel_name"] == "softmax_row"
+    assert osx.softmax_rows_plan(3, 8193)["kernel_name"] == "softmax_split"
     p = osx.softmax_rows_plan(1, 1 << 24)
     assert p["kernel_name"] == "softmax_split" and p["splits"] == (1 << 24) // 16384
     assert osx.softmax_rows_workspace(1, 1 << 24) == p["splits"] * 8

@@ -1,6 +1,7 @@
 """GPU parity of osx_softmax_rows_ex (scale, causal mask, bf16 in/out) against the fp64 oracle.
 
-Covers the one-workgroup-per-row kernel and the split (chunked) kernels,
+Covers the row-in-registers kernels (one wavefront or one workgroup per row)
+and the split (chunked) kernels, at the boundaries between them,
 16-byte and scalar paths (column counts that are and are not multiples of the
 vector width), chunks that are wholly, partly or not masked, and in place.
 Masked outputs must be exactly 0.
@@ -22,6 +23,10 @@ CASES = [  # dtype, rows, cols, causal_period, scale
     ("bf16", 150, 77, 50, 1.0),        # three heads of [50, 77], scalar path (77 % 8 != 0)
     ("f32", 140, 101, 70, 0.3),        # two heads of [70, 101], scalar path (101 % 4 != 0)
     ("bf16", 96, 4096, 48, 0.5),       # vector path, period < cols
+    ("bf16", 33, 2048, 0, 1.0),        # longest wavefront row; 33 rows = 8 full workgroups + 1 row
+    ("f32", 5, 8192, 3, 1.0),          # longest workgroup row, 16-byte path
+    ("f32", 10, 5001, 7, 0.5),         # workgroup row, scalar path
+    ("bf16", 6, 2049, 4, 1.0),         # shortest workgroup row, scalar path
     ("bf16", 2, 65536, 0, 2.0),        # split, 16-byte path, full chunks
     ("bf16", 2, 100003, 0, 1.0),       # split, scalar path, ragged last chunk
     ("f32", 3, 40000, 3, 1.0),         # split: all but the first chunk wholly masked
@@ -78,12 +83,36 @@ def test_softmax_options_large_masked_rows_sampled(osx):
     torch.cuda.synchronize()
     pick = np.array([0, 1, 5000, 16382, 16383, 16384, 16385, 16399])
     got = y[torch.from_numpy(pick).cuda()].cpu().numpy().astype(np.float64)
-    ref = np.stack([oracle.softmax_rows(x[pick[i]:pick[i] + 1], scale=1.0)[0] * 0 for i in range(len(pick))])
+    ref = np.zeros((len(pick), cols))
     for i, r in enumerate(pick):  # row r keeps columns <= r: the oracle on that row's visible prefix
         ref[i, :r + 1] = oracle.softmax_rows(x[r:r + 1, :r + 1])[0]
     _check(got, ref, "f32", 0, "sampled rows")
     for i, r in enumerate(pick):
         assert (got[i, r + 1:] == 0).all()
+
+
+def test_softmax_causal_bf16_workload_sampled(osx):
+    """The timed causal score-row workload at full size (16 heads of [2048, 2048] bf16, scale 1/sqrt(128)),
+    same call as the benchmark: rows sampled from every head, first/last rows of a head included."""
+    w = synth.WORKLOADS["softmax_causal_bf16"]
+    x = synth.softmax_inputs(w)
+    y = osx.softmax_rows(to_dev(x), causal_period=w.causal_period, scale=w.scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(12)
+    pick = np.unique(np.concatenate([[0, 1, 2047, 2048, w.rows - 1], rng.integers(0, w.rows, 59)]))
+    got = to_f64(y[torch.from_numpy(pick).cuda()])
+    # row r of a head keeps columns <= r mod 2048: the oracle on that visible prefix
+    ref = np.stack([_masked_row(x[r], r % w.causal_period, w.scale) for r in pick])
+    _check(got, ref, "bf16", 0, "causal bf16 workload rows")
+    for i, r in enumerate(pick):
+        assert (got[i, r % w.causal_period + 1:] == 0).all()
+
+
+def _masked_row(xr, last, scale):
+    """Oracle softmax of one row whose visible columns are [0, last]; zeros after."""
+    out = np.zeros(xr.shape[0])
+    out[:last + 1] = oracle.softmax_rows(xr[None, :last + 1], scale=scale)[0]
+    return out
 
 
 def test_softmax_options_in_place_bf16(osx):

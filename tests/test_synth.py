@@ -61,3 +61,22 @@ def test_flop_and_byte_counts():
     assert d.bytes() == 2 * (2 * 64 * 32 * 128 + 2 * 64 * 8 * 8192 * 128)
     s = synth.WORKLOADS["softmax_1x16m"]
     assert s.bytes() == 3 * 4 * (1 << 24)
+
+
+def test_causal_softmax_visible_count():
+    """visible() against a direct count of the mask c <= r mod P, and the byte model on top of it."""
+    for rows, cols, period in [(10, 7, 4), (6, 3, 6), (9, 20, 0), (5, 5, 1)]:
+        w = synth.SoftmaxWorkload("t", rows, cols, seed=0, dist="normal", causal_period=period, dtype="bf16")
+        count = sum(1 for r in range(rows) for c in range(cols) if period == 0 or c <= r % period)
+        assert w.visible() == count
+        assert w.bytes() == 2 * (2 * count + rows * cols) and w.bytes(1) == 2 * (count + rows * cols)
+    w = synth.WORKLOADS["softmax_causal_bf16"]
+    assert w.visible() == 16 * 2048 * 2049 // 2
+
+
+def test_causal_softmax_inputs_are_bf16_patterns():
+    w = synth.SoftmaxWorkload("t", 64, 48, seed=7, dist="normal", sigma=2.0, dtype="bf16", causal_period=64)
+    x = synth.softmax_inputs(w)
+    assert x.dtype == np.uint16 and x.shape == (64, 48)
+    f = synth.bf16_bits_to_f32(x)
+    assert np.isfinite(f).all() and 1.5 < f.std() < 2.5
