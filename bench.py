@@ -7,8 +7,10 @@ hot path runs in it.  The headline ``value`` is its causal-adjusted TFLOP/s
 (4*B*Hq*S*S*d / 2 flops per call).  The other hot-path calls are timed in the
 same run and reported under ``also``: GQA decode (GB/s over K/V), the long-row
 softmax and the causal bf16 score-row softmax (GB/s: the visible inputs read
-twice, or once where the row stays in registers, + 1 write), the fp32 4096^2
-attention (TFLOP/s) and the two small latency cases (microseconds).
+twice, or once where the row stays in registers, + 1 write), the two
+three-pass softmax comparators on the long row (with their time relative to
+the two-pass kernel), the fp32 4096^2 attention (TFLOP/s) and the two small
+latency cases (microseconds).
 
 Inputs are seeded synthetic tensors (``synth``), generated on the host and
 copied to HBM before timing.  Durations come from one HIP event pair recorded
@@ -175,6 +177,30 @@ def bench_softmax(torch, osx, args):
             "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", traffic_for("softmax_split"))}
 
 
+def bench_softmax_3pass(torch, osx, args, two_pass_us):
+    """The three-pass comparator designs on the long-row workload, same rotation of buffers as the two-pass line.
+
+    Algorithmic bytes: ATOMIC reads x three times and writes y once (4 x 4N);
+    STASH reads x twice, writes y twice and reads it once (5 x 4N)."""
+    import synth
+    w = synth.WORKLOADS["softmax_1x16m"]
+    x = to_dev(synth.softmax_inputs(w))
+    xs = [x.clone() for _ in range(5)]
+    ys = [torch.empty_like(x) for _ in range(5)]
+    out = {}
+    for name, method, passes in (("atomic", osx.OSX_3PASS_ATOMIC, 4), ("stash", osx.OSX_3PASS_STASH, 5)):
+        ws = torch.empty(osx.softmax_rows_3pass_workspace(w.rows, w.cols, method), dtype=torch.uint8, device="cuda")
+        _, ms = timed(torch, lambda i: osx.softmax_rows_3pass(xs[i % 5], method, out=ys[i % 5], workspace=ws),
+                      args.steps, args.warmup)
+        nbytes = passes * 4.0 * w.rows * w.cols
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[f"softmax_1x16m_3pass_{name}"] = {
+            "workload": w.name, "unit": "GB/s", "value": round(gbs, 1), "call_us": round(ms * 1e3, 2),
+            "bytes_per_call": nbytes, "time_vs_two_pass": round(ms * 1e3 / two_pass_us, 3),
+            "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", None)}
+    return out
+
+
 def bench_softmax_causal(torch, osx, args):
     """Causal bf16 score rows: one workgroup per row reads the visible columns and zero-fills the rest."""
     import synth
@@ -279,6 +305,7 @@ def main():
     if args.only in ("softmax",):
         also["softmax_1x16m"] = bench_softmax(torch, osx, args)
         also["softmax_causal_bf16"] = bench_softmax_causal(torch, osx, args)
+        also.update(bench_softmax_3pass(torch, osx, args, also["softmax_1x16m"]["call_us"]))
         print(json.dumps({"also": also}))
         return
     if args.only in ("f32",):
@@ -298,6 +325,8 @@ def main():
         log(f"[bench] softmax {also['softmax_1x16m']['value']} GB/s")
         also["softmax_causal_bf16"] = bench_softmax_causal(torch, osx, args)
         log(f"[bench] causal bf16 softmax {also['softmax_causal_bf16']['value']} GB/s")
+        also.update(bench_softmax_3pass(torch, osx, args, also["softmax_1x16m"]["call_us"]))
+        log("[bench] three-pass comparators done")
         also["attn_f32_4k_d128"] = bench_f32(torch, osx, args)
         log(f"[bench] fp32 attention {also['attn_f32_4k_d128']['value']} TFLOP/s")
         also.update(bench_small(torch, osx, args))

@@ -164,6 +164,33 @@ int osx_softmax_rows(const float* x, float* y, int64_t rows, int64_t cols, void*
 int osx_softmax_rows_ex(const void* x, void* y, int dtype, int64_t rows, int64_t cols, int64_t causal_period,
                         float scale, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Three-pass row softmax designs, kept as comparators for osx_softmax_rows:
+ * the same y (fp32, x and y [rows, cols] contiguous, y == x allowed), computed
+ * the way page "Softmax 算子的实现与优化" does before its Online Softmax
+ * section.  method:
+ *   OSX_3PASS_ATOMIC  section Baseline: three launches, each reading x -- the
+ *                     max, the sum of e^{x - max}, the normalised output.  The
+ *                     workgroups of a row combine their partials with atomic
+ *                     max / atomic add on one (max, sum) pair per row in the
+ *                     workspace, which a first small launch resets.  The sum's
+ *                     rounding depends on the order the atomics land in.
+ *   OSX_3PASS_STASH   section CUDA 版本: the max; then e^{x - max} written to y
+ *                     and summed; then y multiplied by 1/sum.  Per-chunk
+ *                     partials in the workspace instead of the page's single
+ *                     256-thread block, so long rows use the whole GPU.
+ * Each row is cut into 16384-element chunks, one workgroup per chunk.
+ * Errors as osx_softmax_rows; an unknown method is OSX_EINVAL.
+ */
+#define OSX_3PASS_ATOMIC 1
+#define OSX_3PASS_STASH 2
+
+/* Workspace bytes osx_softmax_rows_3pass needs (always > 0 for a non-empty problem), via *bytes. */
+int osx_softmax_rows_3pass_workspace(int64_t rows, int64_t cols, int method, size_t* bytes);
+
+int osx_softmax_rows_3pass(const float* x, float* y, int64_t rows, int64_t cols, int method, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* osx_status_string(int status);
 

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libosx.so")
 
 OSX_OK, OSX_EINVAL, OSX_EUNSUPPORTED, OSX_EHIP, OSX_EWORKSPACE = 0, -1, -2, -3, -4
 OSX_F32, OSX_BF16 = 0, 1
+OSX_3PASS_ATOMIC, OSX_3PASS_STASH = 1, 2
 KERNELS = {0: "none", 1: "prefill_f32", 2: "prefill_bf16", 3: "decode_bf16", 4: "softmax_row", 5: "softmax_split",
            6: "softmax_wave"}
 
@@ -61,13 +62,16 @@ def _load() -> ctypes.CDLL:
     lib.osx_softmax_rows_workspace.argtypes = [_i64, _i64, ctypes.POINTER(_sz)]
     lib.osx_softmax_rows.argtypes = [_vp, _vp, _i64, _i64, _vp, _sz, _vp]
     lib.osx_softmax_rows_ex.argtypes = [_vp, _vp, _i, _i64, _i64, _i64, _f, _vp, _sz, _vp]
+    lib.osx_softmax_rows_3pass_workspace.argtypes = [_i64, _i64, _i, ctypes.POINTER(_sz)]
+    lib.osx_softmax_rows_3pass.argtypes = [_vp, _vp, _i64, _i64, _i, _vp, _sz, _vp]
     lib.osx_status_string.argtypes = [_i]
     lib.osx_status_string.restype = ctypes.c_char_p
     lib.osx_last_error.argtypes = []
     lib.osx_last_error.restype = ctypes.c_char_p
     lib.osx_version.argtypes = []
     for name in ("osx_attn_plan", "osx_attn_fwd_workspace", "osx_attn_fwd", "osx_attn_fwd_lse", "osx_softmax_rows_plan",
-                 "osx_softmax_rows_workspace", "osx_softmax_rows", "osx_softmax_rows_ex", "osx_version"):
+                 "osx_softmax_rows_workspace", "osx_softmax_rows", "osx_softmax_rows_ex",
+                 "osx_softmax_rows_3pass_workspace", "osx_softmax_rows_3pass", "osx_version"):
         getattr(lib, name).restype = _i
     return lib
 
@@ -223,6 +227,39 @@ def softmax_rows(x, out=None, workspace=None, stream=None, causal_period: int = 
     return out
 
 
+def softmax_rows_3pass_workspace(rows: int, cols: int, method: int) -> int:
+    n = _sz(0)
+    _check(lib.osx_softmax_rows_3pass_workspace(rows, cols, method, ctypes.byref(n)))
+    return n.value
+
+
+def softmax_rows_3pass(x, method: int, out=None, workspace=None, stream=None):
+    """Row softmax of a contiguous float32 CUDA tensor by a three-pass comparator design.
+
+    ``method``: OSX_3PASS_ATOMIC (max, sum of exp and normalise launches, each
+    reading x, merged by atomics) or OSX_3PASS_STASH (max; exp stashed in y and
+    summed; y rescaled).  Same result as :func:`softmax_rows`.
+    """
+    torch = _torch()
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous float32 CUDA tensor")
+    cols = x.shape[-1] if x.dim() else 1
+    rows = x.numel() // cols if cols else 0
+    if out is None:
+        out = torch.empty_like(x)
+    elif out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like x")
+    need = softmax_rows_3pass_workspace(rows, cols, method)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.osx_softmax_rows_3pass(x.data_ptr(), out.data_ptr(), rows, cols, method, ws_ptr, ws_len,
+                                      _stream(x, stream)))
+    return out
+
+
 __all__ = ["attn_fwd", "softmax_rows", "attn_plan", "attn_fwd_workspace", "softmax_rows_plan",
            "softmax_rows_workspace", "status_string", "last_error", "version", "OsxError", "lib", "LIB_PATH",
-           "OSX_F32", "OSX_BF16"]
+           "OSX_F32", "OSX_BF16", "softmax_rows_3pass", "softmax_rows_3pass_workspace", "OSX_3PASS_ATOMIC",
+           "OSX_3PASS_STASH"]

@@ -21,6 +21,7 @@ LIB = os.path.join(HERE, "libosx.so")
 SOURCES = [
     "abi.cpp",
     "softmax_rows.hip",
+    "softmax_3pass.hip",
     "attn_prefill_bf16.hip",
     "attn_prefill_f32.hip",
     "attn_decode_bf16.hip",

@@ -283,6 +283,25 @@ int softmax_rows(const void* x, void* y, int dtype, int64_t rows, int64_t cols, 
   return ok();
 }
 
+// Chunks and workspace of the three-pass comparators.
+int plan_3pass(int64_t rows, int64_t cols, int method, int* splits, int64_t* grid, size_t* ws) {
+  if (method != OSX_3PASS_ATOMIC && method != OSX_3PASS_STASH)
+    return fail(OSX_EINVAL, "method %d: OSX_3PASS_ATOMIC or OSX_3PASS_STASH", method);
+  if (rows < 0 || cols < 0) return fail(OSX_EINVAL, "negative size (rows=%lld cols=%lld)", (long long)rows,
+                                        (long long)cols);
+  *splits = 0;
+  *grid = 0;
+  *ws = 0;
+  if (rows == 0) return ok();
+  if (cols == 0) return fail(OSX_EINVAL, "cols == 0 with rows > 0: softmax over nothing");
+  const int64_t sp = cdiv(cols, osx::kSoftmaxChunk);
+  if (rows * sp > 0x7fffffff) return fail(OSX_EUNSUPPORTED, "problem needs %lld workgroups", (long long)(rows * sp));
+  *splits = (int)sp;
+  *grid = rows * sp;
+  *ws = (size_t)(method == OSX_3PASS_ATOMIC ? rows : rows * sp) * 2 * sizeof(float);
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -295,6 +314,48 @@ int osx_softmax_rows(const float* x, float* y, int64_t rows, int64_t cols, void*
 int osx_softmax_rows_ex(const void* x, void* y, int dtype, int64_t rows, int64_t cols, int64_t causal_period,
                         float scale, void* workspace, size_t workspace_bytes, void* stream) {
   return softmax_rows(x, y, dtype, rows, cols, causal_period, scale, workspace, workspace_bytes, stream);
+}
+
+int osx_softmax_rows_3pass_workspace(int64_t rows, int64_t cols, int method, size_t* bytes) {
+  int splits;
+  int64_t grid;
+  size_t ws = 0;
+  const int st = plan_3pass(rows, cols, method, &splits, &grid, &ws);
+  if (bytes) *bytes = st == OSX_OK ? ws : 0;
+  return st;
+}
+
+int osx_softmax_rows_3pass(const float* x, float* y, int64_t rows, int64_t cols, int method, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  int splits;
+  int64_t grid;
+  size_t need;
+  int st = plan_3pass(rows, cols, method, &splits, &grid, &need);
+  if (st != OSX_OK) return st;
+  if (grid == 0) return ok();
+  if (!x || !y) return fail(OSX_EINVAL, "null x or y pointer");
+  const size_t n = (size_t)rows * (size_t)cols * sizeof(float);
+  if (x != y && overlap(x, n, y, n)) return fail(OSX_EINVAL, "x and y overlap without being the same buffer");
+  if (!workspace || workspace_bytes < need)
+    return fail(OSX_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : (size_t)0,
+                need);
+  if (overlap(workspace, need, x, n) || overlap(workspace, need, y, n))
+    return fail(OSX_EINVAL, "workspace overlaps x or y");
+  osx::Softmax3PassArgs a;
+  a.x = x;
+  a.y = y;
+  a.rows = rows;
+  a.cols = cols;
+  a.method = method;
+  a.splits = splits;
+  a.chunk = osx::kSoftmaxChunk;
+  a.grid = grid;
+  a.workspace = workspace;
+  a.stream = (hipStream_t)stream;
+  hipError_t e = osx::launch_softmax_3pass(a);
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) return fail(OSX_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
 }
 
 const char* osx_status_string(int status) {

@@ -53,9 +53,22 @@ struct SoftmaxArgs {
   osx_plan plan;
 };
 
+struct Softmax3PassArgs {
+  const void* x;
+  void* y;
+  int64_t rows, cols;
+  int method;      // OSX_3PASS_ATOMIC or OSX_3PASS_STASH
+  int splits;      // chunks per row
+  int64_t chunk;   // elements per chunk (one workgroup each)
+  int64_t grid;    // rows * splits
+  void* workspace; // ATOMIC: (m, l) per row; STASH: (max, sum) per chunk; fp32
+  hipStream_t stream;
+};
+
 hipError_t launch_prefill_bf16(const AttnArgs& a);
 hipError_t launch_prefill_f32(const AttnArgs& a);
 hipError_t launch_decode_bf16(const AttnArgs& a);
 hipError_t launch_softmax_rows(const SoftmaxArgs& a);
+hipError_t launch_softmax_3pass(const Softmax3PassArgs& a);
 
 }  // namespace osx

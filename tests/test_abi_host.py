@@ -149,3 +149,20 @@ def test_softmax_rows_ex_rejects_before_launch():
                                    None) == osx.OSX_EINVAL
     assert lib.osx_softmax_rows_ex(x, y, BF16, 1, 1 << 20, 0, 1.0, None, 0, None) == osx.OSX_EWORKSPACE
     assert lib.osx_softmax_rows_ex(None, None, BF16, 0, 16, 3, 1.0, None, 0, None) == 0
+
+
+def test_softmax_3pass_workspace_and_rejects():
+    lib = osx.lib
+    A, S = osx.OSX_3PASS_ATOMIC, osx.OSX_3PASS_STASH
+    assert osx.softmax_rows_3pass_workspace(3, 100, A) == 3 * 8            # (max, sum) per row
+    assert osx.softmax_rows_3pass_workspace(3, 40000, S) == 3 * 3 * 8      # (max, sum) per 16384-element chunk
+    assert osx.softmax_rows_3pass_workspace(0, 100, S) == 0
+    x, y, ws = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x900000), ctypes.c_void_p(0x2000000)
+    assert lib.osx_softmax_rows_3pass(x, y, 4, 16, 3, ws, 64, None) == osx.OSX_EINVAL     # method
+    assert lib.osx_softmax_rows_3pass(x, y, 4, 0, A, ws, 64, None) == osx.OSX_EINVAL      # empty rows
+    assert lib.osx_softmax_rows_3pass(x, y, -1, 16, A, ws, 64, None) == osx.OSX_EINVAL
+    assert lib.osx_softmax_rows_3pass(x, y, 4, 16, A, None, 0, None) == osx.OSX_EWORKSPACE
+    assert lib.osx_softmax_rows_3pass(x, y, 4, 16, A, ws, 31, None) == osx.OSX_EWORKSPACE  # needs 32
+    assert lib.osx_softmax_rows_3pass(x, ctypes.c_void_p(0x100000 + 16), 4, 16, S, ws, 64, None) == osx.OSX_EINVAL
+    assert lib.osx_softmax_rows_3pass(x, y, 4, 16, S, ctypes.c_void_p(0x100000 + 8), 64, None) == osx.OSX_EINVAL
+    assert lib.osx_softmax_rows_3pass(None, None, 0, 16, S, None, 0, None) == 0             # no work
