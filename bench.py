@@ -10,7 +10,8 @@ softmax and the causal bf16 score-row softmax (GB/s: the visible inputs read
 twice, or once where the row stays in registers, + 1 write), the two
 three-pass softmax comparators on the long row (with their time relative to
 the two-pass kernel), the fp32 4096^2 attention (TFLOP/s) and the two small
-latency cases (microseconds).
+latency cases (microseconds), and the unfused three-kernel attention
+comparator on the prefill workload (its time relative to the fused call).
 
 Inputs are seeded synthetic tensors (``synth``), generated on the host and
 copied to HBM before timing.  Durations come from one HIP event pair recorded
@@ -49,7 +50,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--only", default="all", choices=["all", "prefill", "decode", "softmax", "f32", "small", "copy"],
+    p.add_argument("--only", default="all",
+                   choices=["all", "prefill", "unfused", "decode", "softmax", "f32", "small", "copy"],
                    help="time one workload only (for profiler runs)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle timing sample")
@@ -137,8 +139,29 @@ def bench_prefill(torch, osx, args):
     wall, kern_ms = timed(torch, lambda i: osx.attn_fwd(q, k, v, causal=True, out=out), args.steps, args.warmup)
     tflops = w.flops() / (kern_ms * 1e-3) / 1e12
     res = {"wall_s": wall, "ms_per_step": wall / args.steps * 1e3, "kernel_ms": kern_ms, "tflops": tflops,
-           "roofline": roofline("mfma", tflops, PEAK_BF16_TFLOPS, "TFLOP/s", traffic_for("prefill_bf16_kernel"))}
+           "roofline": roofline("mfma", tflops, PEAK_BF16_TFLOPS, "TFLOP/s", traffic_for("prefill_bf16_kernel")),
+           "qkv": (q, k, v)}
     return res, t, w
+
+
+def bench_unfused(torch, osx, args, q, k, v, w, fused_ms):
+    """The unfused three-kernel comparator on the prefill workload: S = scale q k^T to HBM (fp32), softmax in
+    place, P v.  Its HBM traffic is dominated by four passes over S (written, read and rewritten by the
+    softmax, read by the P v product): 16 bytes per score, plus q, k, v, o once."""
+    out = torch.empty_like(q)
+    ws = torch.empty(osx.attn_fwd_unfused_workspace(osx.OSX_BF16, w.batch, w.heads_q, w.heads_kv, w.seq_q, w.seq_k,
+                                                    w.head_dim, True), dtype=torch.uint8, device="cuda")
+    steps = max(3, args.steps // 4)
+    _, ms = timed(torch, lambda i: osx.attn_fwd_unfused(q, k, v, causal=True, out=out, workspace=ws), steps,
+                  args.warmup)
+    scores = float(w.batch * w.heads_q * w.seq_q * w.seq_k)
+    nbytes = 16.0 * scores + w.bytes()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": w.name, "unit": "GB/s", "value": round(gbs, 1), "call_us": round(ms * 1e3, 2),
+            "bytes_per_call": nbytes, "score_matrix_bytes": 4.0 * scores,
+            "tflops_causal_adjusted": round(w.flops() / (ms * 1e-3) / 1e12, 2),
+            "time_vs_fused": round(ms / fused_ms, 2),
+            "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", None)}
 
 
 def bench_decode(torch, osx, args):
@@ -318,6 +341,15 @@ def main():
 
     head, t, w = bench_prefill(torch, osx, args)
     log(f"[bench] prefill {head['tflops']:.1f} TFLOP/s ({head['kernel_ms']:.3f} ms per call)")
+    if args.only in ("all", "unfused"):
+        also["attn_unfused_gqa_prefill_bf16"] = bench_unfused(torch, osx, args, *head.pop("qkv"), w,
+                                                              head["kernel_ms"])
+        log(f"[bench] unfused comparator {also['attn_unfused_gqa_prefill_bf16']['call_us']} us")
+    else:
+        head.pop("qkv")
+    if args.only == "unfused":
+        print(json.dumps({"also": also}))
+        return
     if args.only == "all":
         also["gqa_decode_bf16"] = bench_decode(torch, osx, args)
         log(f"[bench] decode {also['gqa_decode_bf16']['value']} GB/s")

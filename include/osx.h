@@ -122,6 +122,29 @@ int osx_attn_fwd_lse(const void* q, const void* k, const void* v, void* o, float
                      int heads_q, int heads_kv, int seq_q, int seq_k, int head_dim, int causal, float scale,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * osx_attn_fwd_unfused -- the same O as osx_attn_fwd, computed the unfused way
+ * as a comparator: the three kernels of page "从零开始写Qwen3（五-其一）使用Triton
+ * 实现自注意力" (sections 免转置矩阵乘法, softmax的triton实现, 串起来):
+ *   1. S = scale * Q K^T, written as an fp32 [batch * heads_q, seq_q, seq_k]
+ *      matrix in the workspace (K read along head_dim, not transposed);
+ *   2. the row softmax of S in place (osx_softmax_rows_ex, fp32; causal keeps
+ *      key <= query);
+ *   3. O = P V, with P rounded to bf16 for the products (fp32 accumulation).
+ * All keys are multiplied, masked ones included, as on the page.
+ *
+ * dtype must be OSX_BF16 (else OSX_EUNSUPPORTED); head_dim 64 or 128;
+ * seq_q * seq_k at most 2^29 (OSX_EUNSUPPORTED above).  Layouts, GQA, causal
+ * and scale as osx_attn_fwd.  workspace: osx_attn_fwd_unfused_workspace bytes
+ * (the score matrix, 4 bytes per score, plus the softmax's own workspace);
+ * it must not overlap q, k, v or o.  Errors as osx_attn_fwd.
+ */
+int osx_attn_fwd_unfused_workspace(int dtype, int batch, int heads_q, int heads_kv, int seq_q, int seq_k,
+                                   int head_dim, int causal, size_t* bytes);
+int osx_attn_fwd_unfused(const void* q, const void* k, const void* v, void* o, int dtype, int batch, int heads_q,
+                         int heads_kv, int seq_q, int seq_k, int head_dim, int causal, float scale, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
 /* osx_softmax_rows_plan -- kernel choice for x[rows, cols]; no HIP calls. */
 int osx_softmax_rows_plan(int64_t rows, int64_t cols, osx_plan* out);
 

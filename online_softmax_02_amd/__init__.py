@@ -62,6 +62,8 @@ def _load() -> ctypes.CDLL:
     lib.osx_softmax_rows_workspace.argtypes = [_i64, _i64, ctypes.POINTER(_sz)]
     lib.osx_softmax_rows.argtypes = [_vp, _vp, _i64, _i64, _vp, _sz, _vp]
     lib.osx_softmax_rows_ex.argtypes = [_vp, _vp, _i, _i64, _i64, _i64, _f, _vp, _sz, _vp]
+    lib.osx_attn_fwd_unfused_workspace.argtypes = attn_shape + [ctypes.POINTER(_sz)]
+    lib.osx_attn_fwd_unfused.argtypes = [_vp, _vp, _vp, _vp] + attn_shape + [_f, _vp, _sz, _vp]
     lib.osx_softmax_rows_3pass_workspace.argtypes = [_i64, _i64, _i, ctypes.POINTER(_sz)]
     lib.osx_softmax_rows_3pass.argtypes = [_vp, _vp, _i64, _i64, _i, _vp, _sz, _vp]
     lib.osx_status_string.argtypes = [_i]
@@ -71,7 +73,8 @@ def _load() -> ctypes.CDLL:
     lib.osx_version.argtypes = []
     for name in ("osx_attn_plan", "osx_attn_fwd_workspace", "osx_attn_fwd", "osx_attn_fwd_lse", "osx_softmax_rows_plan",
                  "osx_softmax_rows_workspace", "osx_softmax_rows", "osx_softmax_rows_ex",
-                 "osx_softmax_rows_3pass_workspace", "osx_softmax_rows_3pass", "osx_version"):
+                 "osx_softmax_rows_3pass_workspace", "osx_softmax_rows_3pass", "osx_attn_fwd_unfused_workspace",
+                 "osx_attn_fwd_unfused", "osx_version"):
         getattr(lib, name).restype = _i
     return lib
 
@@ -227,6 +230,46 @@ def softmax_rows(x, out=None, workspace=None, stream=None, causal_period: int = 
     return out
 
 
+def attn_fwd_unfused_workspace(dtype: int, batch: int, heads_q: int, heads_kv: int, seq_q: int, seq_k: int,
+                               head_dim: int, causal: bool = False) -> int:
+    n = _sz(0)
+    _check(lib.osx_attn_fwd_unfused_workspace(dtype, batch, heads_q, heads_kv, seq_q, seq_k, head_dim, int(causal),
+                                              ctypes.byref(n)))
+    return n.value
+
+
+def attn_fwd_unfused(q, k, v, causal: bool = False, scale: float | None = None, out=None, workspace=None,
+                     stream=None):
+    """The same O as :func:`attn_fwd` (bf16 only), computed by the unfused comparator: the score matrix
+    S = scale * q k^T is written to the workspace (fp32, 4 bytes per score), softmaxed in place, then
+    multiplied by v.  Shapes as :func:`attn_fwd`."""
+    torch = _torch()
+    squeeze = q.dim() == 2
+    if squeeze:
+        q, k, v = q[None, None], k[None, None], v[None, None]
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dim() != 4 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-D CUDA tensor")
+    if k.shape != v.shape or q.dtype != k.dtype or k.dtype != v.dtype:
+        raise ValueError("k and v must match, and q, k, v share one dtype")
+    B, Hq, Sq, D = q.shape
+    _, Hkv, Sk, _ = k.shape
+    code = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    need = attn_fwd_unfused_workspace(code, B, Hq, Hkv, Sq, Sk, D, causal)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.osx_attn_fwd_unfused(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), code, B, Hq, Hkv, Sq,
+                                    Sk, D, int(causal), float(scale) if scale else 0.0, ws_ptr, ws_len,
+                                    _stream(q, stream)))
+    return out[0, 0] if squeeze else out
+
+
 def softmax_rows_3pass_workspace(rows: int, cols: int, method: int) -> int:
     n = _sz(0)
     _check(lib.osx_softmax_rows_3pass_workspace(rows, cols, method, ctypes.byref(n)))
@@ -262,4 +305,4 @@ def softmax_rows_3pass(x, method: int, out=None, workspace=None, stream=None):
 __all__ = ["attn_fwd", "softmax_rows", "attn_plan", "attn_fwd_workspace", "softmax_rows_plan",
            "softmax_rows_workspace", "status_string", "last_error", "version", "OsxError", "lib", "LIB_PATH",
            "OSX_F32", "OSX_BF16", "softmax_rows_3pass", "softmax_rows_3pass_workspace", "OSX_3PASS_ATOMIC",
-           "OSX_3PASS_STASH"]
+           "OSX_3PASS_STASH", "attn_fwd_unfused", "attn_fwd_unfused_workspace"]

@@ -25,6 +25,7 @@ SOURCES = [
     "attn_prefill_bf16.hip",
     "attn_prefill_f32.hip",
     "attn_decode_bf16.hip",
+    "attn_unfused.hip",
 ]
 
 ARCH = "gfx950"

@@ -302,6 +302,32 @@ int plan_3pass(int64_t rows, int64_t cols, int method, int* splits, int64_t* gri
   return ok();
 }
 
+// Unfused attention: the [B*Hq, Sq, Sk] fp32 score matrix, then the row
+// softmax's own workspace (rows longer than one workgroup holds).
+int plan_unfused(int dtype, int batch, int heads_q, int heads_kv, int seq_q, int seq_k, int head_dim, int causal,
+                 size_t* s_bytes, size_t* total) {
+  *s_bytes = 0;
+  *total = 0;
+  osx_plan p;
+  int st = plan_attn(dtype, batch, heads_q, heads_kv, seq_q, seq_k, head_dim, causal, &p);
+  if (st != OSX_OK) return st;
+  if (p.kernel == OSX_KERNEL_NONE) return ok();
+  if (dtype != OSX_BF16) return fail(OSX_EUNSUPPORTED, "unfused attention takes bf16 q, k, v, o");
+  if ((int64_t)batch * heads_q > 65535)
+    return fail(OSX_EUNSUPPORTED, "unfused attention: batch * heads_q = %lld exceeds 65535",
+                (long long)batch * heads_q);
+  if ((int64_t)seq_q * seq_k > (1LL << 29))
+    return fail(OSX_EUNSUPPORTED, "unfused attention: seq_q * seq_k = %lld exceeds 2^29 scores per head",
+                (long long)seq_q * seq_k);
+  const int64_t rows = (int64_t)batch * heads_q * seq_q;
+  osx_plan sp;
+  st = plan_softmax(rows, seq_k, &sp);
+  if (st != OSX_OK) return st;
+  *s_bytes = (size_t)rows * (size_t)seq_k * sizeof(float);
+  *total = *s_bytes + sp.workspace_bytes;
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -314,6 +340,58 @@ int osx_softmax_rows(const float* x, float* y, int64_t rows, int64_t cols, void*
 int osx_softmax_rows_ex(const void* x, void* y, int dtype, int64_t rows, int64_t cols, int64_t causal_period,
                         float scale, void* workspace, size_t workspace_bytes, void* stream) {
   return softmax_rows(x, y, dtype, rows, cols, causal_period, scale, workspace, workspace_bytes, stream);
+}
+
+int osx_attn_fwd_unfused_workspace(int dtype, int batch, int heads_q, int heads_kv, int seq_q, int seq_k,
+                                   int head_dim, int causal, size_t* bytes) {
+  size_t s_bytes, total;
+  const int st = plan_unfused(dtype, batch, heads_q, heads_kv, seq_q, seq_k, head_dim, causal, &s_bytes, &total);
+  if (bytes) *bytes = st == OSX_OK ? total : 0;
+  return st;
+}
+
+int osx_attn_fwd_unfused(const void* q, const void* k, const void* v, void* o, int dtype, int batch, int heads_q,
+                         int heads_kv, int seq_q, int seq_k, int head_dim, int causal, float scale, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  size_t s_bytes, need;
+  int st = plan_unfused(dtype, batch, heads_q, heads_kv, seq_q, seq_k, head_dim, causal, &s_bytes, &need);
+  if (st != OSX_OK) return st;
+  if (need == 0) return ok();
+  if (!q || !k || !v || !o) return fail(OSX_EINVAL, "null q, k, v or o pointer");
+  if (!workspace || workspace_bytes < need)
+    return fail(OSX_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : (size_t)0,
+                need);
+  if (!(scale > 0.0f) || !std::isfinite(scale)) scale = 1.0f / std::sqrt((float)head_dim);
+  const size_t nq = (size_t)batch * heads_q * seq_q * head_dim * 2;
+  const size_t nkv = (size_t)batch * heads_kv * seq_k * head_dim * 2;
+  if (overlap(o, nq, q, nq) || overlap(o, nq, k, nkv) || overlap(o, nq, v, nkv) || overlap(o, nq, workspace, need))
+    return fail(OSX_EINVAL, "output overlaps an input or the workspace");
+  if (overlap(workspace, need, q, nq) || overlap(workspace, need, k, nkv) || overlap(workspace, need, v, nkv))
+    return fail(OSX_EINVAL, "workspace overlaps an input");
+  osx::AttnArgs a = {};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.batch = batch;
+  a.heads_q = heads_q;
+  a.heads_kv = heads_kv;
+  a.seq_q = seq_q;
+  a.seq_k = seq_k;
+  a.head_dim = head_dim;
+  a.causal = causal ? 1 : 0;
+  a.stream = (hipStream_t)stream;
+  float* S = static_cast<float*>(workspace);
+  hipError_t e = osx::launch_unfused_scores(a, S, scale);
+  if (e != hipSuccess) return fail(OSX_EHIP, "score kernel launch failed: %s", hipGetErrorString(e));
+  // Row r of S is query r mod seq_q of its head; causal keeps keys <= that query.
+  st = softmax_rows(S, S, OSX_F32, (int64_t)batch * heads_q * seq_q, seq_k, causal && seq_q > 1 ? seq_q : 0, 1.0f,
+                    static_cast<char*>(workspace) + s_bytes, need - s_bytes, stream);
+  if (st != OSX_OK) return st;
+  e = osx::launch_unfused_pv(a, S);
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) return fail(OSX_EHIP, "P V kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
 }
 
 int osx_softmax_rows_3pass_workspace(int64_t rows, int64_t cols, int method, size_t* bytes) {

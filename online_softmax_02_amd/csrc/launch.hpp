@@ -69,6 +69,8 @@ hipError_t launch_prefill_bf16(const AttnArgs& a);
 hipError_t launch_prefill_f32(const AttnArgs& a);
 hipError_t launch_decode_bf16(const AttnArgs& a);
 hipError_t launch_softmax_rows(const SoftmaxArgs& a);
+hipError_t launch_unfused_scores(const AttnArgs& a, float* s, float scale);  // bf16, head_dim 64 or 128
+hipError_t launch_unfused_pv(const AttnArgs& a, const float* p);
 hipError_t launch_softmax_3pass(const Softmax3PassArgs& a);
 
 }  // namespace osx
