@@ -8,7 +8,8 @@
 //    of that KV head are packed into the 16 columns of a 16x16x32 MFMA tile, so
 //    every K/V byte is read once and serves all G heads.
 //  * Each of the 4 wavefronts walks its own 32-key blocks of the split with
-//    16-byte loads; two workgroups per CU keep enough loads in flight.  K feeds S^T = K Q^T directly from registers; V is written
+//    16-byte loads, the next block loading while the current one is computed;
+//    two workgroups per CU.  K feeds S^T = K Q^T directly from registers; V is written
 //    to the wavefront's LDS slice transposed (keys permuted so each lane's 8
 //    keys are one 16-byte read) and feeds O^T += V^T P^T.
 //  * The 4 wavefront states are merged in LDS and written as one partial
@@ -35,6 +36,10 @@ struct DecTile {
 };
 
 __device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+// K and V are read exactly once: non-temporal buffer loads (cache policy 2).
+__device__ __forceinline__ u32x4 ld16_nt(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 2);
+}
 
 // V^T row (64 bytes = 4 chunks of 8 keys) swizzle: 16 consecutive rows hit 16
 // distinct bank groups.
@@ -46,8 +51,8 @@ struct Regs {
   u32x4 v[DecTile<D>::VU][4];  // [unit][key in quad]
 };
 
-// Keys past Sk read as zeros (buffer range); keys past the split's end are
-// real data that the score mask removes (their weights are exactly 0).
+// Keys past the split's end (and so past Sk) read as zeros through the buffer
+// range; the score mask removes them (their weights are exactly 0).
 template <int D>
 __device__ __forceinline__ void load_regs(Regs<D>& R, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr, int j0,
                                           int lane) {
@@ -57,14 +62,14 @@ __device__ __forceinline__ void load_regs(Regs<D>& R, __amdgpu_buffer_rsrc_t kr,
   for (int t = 0; t < 2; ++t) {
     const int j = j0 + 16 * t + l16;
 #pragma unroll
-    for (int kc = 0; kc < T::KC; ++kc) R.k[t][kc] = buf_ld16(kr, (uint32_t)(j * D + 32 * kc + 8 * grp) * 2);
+    for (int kc = 0; kc < T::KC; ++kc) R.k[t][kc] = ld16_nt(kr, (uint32_t)(j * D + 32 * kc + 8 * grp) * 2);
   }
 #pragma unroll
   for (int r = 0; r < T::VU; ++r) {
     const int u = lane + kWaveSize * r;
     const int kq = u / T::CH, ch = u % T::CH;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) R.v[r][jj] = buf_ld16(vr, (uint32_t)((j0 + 4 * kq + jj) * D + 8 * ch) * 2);
+    for (int jj = 0; jj < 4; ++jj) R.v[r][jj] = ld16_nt(vr, (uint32_t)((j0 + 4 * kq + jj) * D + 8 * ch) * 2);
   }
 }
 
@@ -92,8 +97,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void decode_bf16_kernel(
   int k_end = k_begin + keys_per_split;
   if (k_end > Sk) k_end = Sk;
 
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc(Kg + (size_t)bkv * Sk * D, (uint32_t)Sk * D * 2);
-  const __amdgpu_buffer_rsrc_t vr = make_rsrc(Vg + (size_t)bkv * Sk * D, (uint32_t)Sk * D * 2);
+  // The resources end at the split's last key: loads past it return zeros
+  // without touching memory, so the stream below can prefetch one block past
+  // its end unconditionally (those keys are masked).
+  const int k_lim = k_end > k_begin ? k_end : k_begin;
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(Kg + (size_t)bkv * Sk * D, (uint32_t)k_lim * D * 2);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(Vg + (size_t)bkv * Sk * D, (uint32_t)k_lim * D * 2);
 
   // Q^T as the B operand: column l16 is query head kvh*G + l16 (zero past G).
   bf16x8 qop[T::KC];
@@ -188,11 +197,27 @@ __global__ __launch_bounds__(kAttnThreads, 2) void decode_bf16_kernel(
   };
 
   // ---- stream this wavefront's blocks: k_begin + BN*(wave + 4i) ----
-  for (int j0 = k_begin + BN * wave; j0 < k_end; j0 += BN * kAttnWaves) {
-    Regs<D> r;
-    load_regs<D>(r, kr, vr, j0, lane);
-    compute(r, j0);
+  // Two register sets: block i + 1 is loading while block i is computed.  The
+  // loop runs over pairs of blocks with no exit in between (the last prefetch
+  // of an even count lies past the split and reads zeros without touching
+  // memory); an odd last block follows it.  sched_barrier keeps each prefetch
+  // ahead of the compute, which would otherwise be hoisted above it and then
+  // wait for the prefetch too.
+  constexpr int kStep = BN * kAttnWaves;
+  int j0 = k_begin + BN * wave;
+  const int nblk = j0 < k_end ? (k_end - j0 + kStep - 1) / kStep : 0;
+  Regs<D> ra, rb;
+  load_regs<D>(ra, kr, vr, j0, lane);
+  for (int pair = 0; pair < nblk / 2; ++pair) {
+    load_regs<D>(rb, kr, vr, j0 + kStep, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(ra, j0);
+    load_regs<D>(ra, kr, vr, j0 + 2 * kStep, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(rb, j0 + kStep);
+    j0 += 2 * kStep;
   }
+  if (nblk & 1) compute(ra, j0);
 
   // ---- merge the 4 wavefront states in LDS ----
   l_run += __shfl_xor(l_run, 16, 64);
