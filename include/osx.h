@@ -40,7 +40,8 @@ extern "C" {
 /* Status codes. */
 #define OSX_OK 0
 #define OSX_EINVAL (-1)      /* bad argument: null pointer, negative size, Hq % Hkv != 0, empty softmax, overlap */
-#define OSX_EUNSUPPORTED (-2) /* valid request outside what the kernels implement (head_dim, causal with Sq != Sk) */
+#define OSX_EUNSUPPORTED (-2) /* valid request outside what the kernels implement (head_dim, causal with Sq != Sk,
+                                 one head's Q/K/V of 2^31 bytes or more) */
 #define OSX_EHIP (-3)        /* the HIP runtime reported an error at launch */
 #define OSX_EWORKSPACE (-4)  /* workspace missing or smaller than the size the query returns */
 

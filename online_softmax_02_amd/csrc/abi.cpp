@@ -49,6 +49,15 @@ int plan_attn(int dtype, int batch, int heads_q, int heads_kv, int seq_q, int se
     return fail(OSX_EUNSUPPORTED, "fp32 head_dim %d: must be a multiple of 4 and at most 128", head_dim);
   if (dtype == OSX_BF16 && head_dim != 64 && head_dim != 128)
     return fail(OSX_EUNSUPPORTED, "bf16 head_dim %d: must be 64 or 128", head_dim);
+  // The kernels address one head's Q, K, V or O through 32-bit buffer ranges and
+  // 32-bit element offsets: each must stay below 2^31 bytes.
+  {
+    const int64_t es = dtype == OSX_BF16 ? 2 : 4;
+    const int64_t longest = (int64_t)(seq_q > seq_k ? seq_q : seq_k) * head_dim * es;
+    if (longest >= (1LL << 31))
+      return fail(OSX_EUNSUPPORTED, "one head of %lld positions x %d dims is %lld bytes: at most 2^31 - 1",
+                  (long long)(seq_q > seq_k ? seq_q : seq_k), head_dim, (long long)longest);
+  }
   if (causal && seq_q > 1 && seq_q != seq_k)
     return fail(OSX_EUNSUPPORTED, "causal with seq_q (%d) != seq_k (%d): mask alignment is not defined", seq_q,
                 seq_k);

@@ -166,3 +166,14 @@ def test_softmax_3pass_workspace_and_rejects():
     assert lib.osx_softmax_rows_3pass(x, ctypes.c_void_p(0x100000 + 16), 4, 16, S, ws, 64, None) == osx.OSX_EINVAL
     assert lib.osx_softmax_rows_3pass(x, y, 4, 16, S, ctypes.c_void_p(0x100000 + 8), 64, None) == osx.OSX_EINVAL
     assert lib.osx_softmax_rows_3pass(None, None, 0, 16, S, None, 0, None) == 0             # no work
+
+
+def test_plan_rejects_heads_beyond_32_bit_addressing():
+    """One head's K/V must stay below 2^31 bytes (the kernels' buffer ranges and offsets are 32-bit)."""
+    with pytest.raises(osx.OsxError) as e:
+        osx.attn_plan(BF16, 1, 1, 1, 1 << 23, 1 << 23, 128)  # 2^23 * 128 * 2 = 2^31 bytes
+    assert e.value.status == osx.OSX_EUNSUPPORTED
+    with pytest.raises(osx.OsxError):
+        osx.attn_plan(F32, 1, 1, 1, 1, 1 << 22, 128)  # decode-shaped, K of 2^31 bytes
+    assert osx.attn_plan(BF16, 1, 1, 1, 1, (1 << 23) - 1, 128)["kernel_name"] == "decode_bf16"
+    assert osx.attn_plan(F32, 1, 1, 1, 1000, (1 << 22) - 1, 128)["kernel_name"] == "prefill_f32"

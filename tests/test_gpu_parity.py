@@ -268,3 +268,30 @@ def test_single_hip_runtime_in_process(osx):
     with open("/proc/self/maps") as f:
         libs = {line.split()[-1] for line in f if "libamdhip64" in line}
     assert len(libs) == 1, libs
+
+
+def test_decode_longest_supported_kv(osx):
+    """Decode at the longest K/V the ABI accepts for d = 128 bf16: 2^23 - 1 keys, 2 GiB each for K and V.
+
+    The oracle cannot hold 8M keys in fp64, so this checks a property that holds at any size: the last key
+    is planted so that its scaled score is s* = 30 while every other score is ~0, so its weight is
+    1 - O(Sk e^-30) ~ 1 - 1e-6 and O equals V[Sk - 1] within the bf16 bar, and the log-sum-exp is
+    s* + O(1e-6).  The planted key sits at the very end of the 2 GiB ranges the kernel addresses.
+    """
+    Sk, D = (1 << 23) - 1, 128
+    print(f"case decode longest kv Sk={Sk}", flush=True)
+    gen = torch.Generator(device="cuda").manual_seed(23)
+    q1 = torch.randn(D, device="cuda", generator=gen).to(torch.bfloat16)
+    q = q1.expand(1, 4, 1, D).contiguous()
+    k = (torch.randn(1, 1, Sk, D, device="cuda", generator=gen, dtype=torch.bfloat16) * 0.01).to(torch.bfloat16)
+    v = torch.randn(1, 1, Sk, D, device="cuda", generator=gen, dtype=torch.bfloat16)
+    qf = q1.double().cpu().numpy()
+    k[0, 0, Sk - 1] = torch.from_numpy(30.0 * np.sqrt(D) * qf / (qf @ qf)).to("cuda").to(torch.bfloat16)
+    o, lse = osx.attn_fwd(q, k, v, return_lse=True)
+    torch.cuda.synchronize()
+    s_star = float(qf @ k[0, 0, Sk - 1].double().cpu().numpy()) / np.sqrt(D)
+    assert abs(s_star - 30.0) < 0.5
+    want = np.broadcast_to(to_f64(v[0, 0, Sk - 1]), (4, D))
+    check(to_f64(o)[0, :, 0], want, "bf16", "planted last key")
+    assert np.abs(lse.double().cpu().numpy()[0, :, 0] - s_star).max() < 1e-3
+    del k, v
