@@ -284,10 +284,23 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(const float* __restric
   const float L = wave_sum(l_s * w_s);
   const float* pa = ws_acc + row * splits * d;
   float a0 = 0.f, a1 = 0.f;
-  for (int s = 0; s < splits; ++s) {
-    const float w = __shfl(w_s, s, 64);
-    if (lane < d) a0 += pa[(int64_t)s * d + lane] * w;
-    if (lane + 64 < d) a1 += pa[(int64_t)s * d + lane + 64] * w;
+  // Eight slices' partial outputs are loaded before any is used, so their load
+  // latencies overlap instead of adding up.
+  constexpr int kBatch = 8;
+  for (int s0 = 0; s0 < splits; s0 += kBatch) {
+    float x0[kBatch], x1[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int s = s0 + b;
+      x0[b] = s < splits && lane < d ? pa[(int64_t)s * d + lane] : 0.f;
+      x1[b] = s < splits && lane + 64 < d ? pa[(int64_t)s * d + lane + 64] : 0.f;
+    }
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const float w = __shfl(w_s, (s0 + b) & 63, 64);  // 0 past the last slice (w_s is 0 there)
+      a0 += x0[b] * w;
+      a1 += x1[b] * w;
+    }
   }
   const float inv = 1.0f / L;
   if (Lse && lane == 0) Lse[row] = (M + log2f(L)) * kLn2;
