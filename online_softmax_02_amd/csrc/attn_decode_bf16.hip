@@ -275,14 +275,35 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restri
   const float* ws_ml = ws;
   const float* ws_acc = ws + 2 * n_part;
   const int dd = threadIdx.x;
-  float M = kNegInf;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, ws_ml[((size_t)(bkv * splits + s) * G + g) * 2]);
-  float l = 0.f, a = 0.f;
-  for (int s = 0; s < splits; ++s) {
-    const size_t p = (size_t)(bkv * splits + s) * G + g;
-    const float f = exp2_fast(ws_ml[p * 2] - M);
-    l += ws_ml[p * 2 + 1] * f;
-    a += ws_acc[p * D + dd] * f;
+  // One pass over the splits in batches of 8, each batch's loads issued before
+  // any is used; the running (M, l, a) absorbs a batch with the same rule.
+  constexpr int kBatch = 8;
+  float M = kNegInf, l = 0.f, a = 0.f;
+  for (int s0 = 0; s0 < splits; s0 += kBatch) {
+    float ms[kBatch], ls[kBatch], as[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const bool in = s0 + b < splits;
+      const size_t p = (size_t)(bkv * splits + (in ? s0 + b : s0)) * G + g;
+      ms[b] = in ? ws_ml[p * 2] : kNegInf;
+      ls[b] = in ? ws_ml[p * 2 + 1] : 0.f;
+      as[b] = in ? ws_acc[p * D + dd] : 0.f;
+    }
+    float mb = ms[0];
+#pragma unroll
+    for (int b = 1; b < kBatch; ++b) mb = fmaxf(mb, ms[b]);
+    const float mn = fmaxf(M, mb);
+    if (mn == kNegInf) continue;  // no key seen yet
+    const float r = exp2_fast(M - mn);  // 0 while M is -inf
+    l *= r;
+    a *= r;
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const float f = exp2_fast(ms[b] - mn);  // 0 for an empty or missing split
+      l += ls[b] * f;
+      a += as[b] * f;
+    }
+    M = mn;
   }
   const float o = a / l;
   // log sum_j exp(scale * s_j) = ln 2 * (M + log2 l), M in the log2 domain
