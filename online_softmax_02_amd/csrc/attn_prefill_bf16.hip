@@ -495,10 +495,13 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
     // Always the full MFMA phase: a block this wavefront cannot see has zero
     // weights (its PV adds nothing) and its scores go unused.
     gemm_fast(k_stage[P], v_stage[P], k_stage[(P + 3) % kStages], v_stage[(P + 3) % kStages]);
-    advance(cur_v);
-    advance(cur_k);
     phase_barrier();
     __builtin_amdgcn_s_setprio(0);
+    // The load cursors step on here, in the softmax phase, which has slack:
+    // their scalar arithmetic (the next tile's indices) would otherwise sit at
+    // the end of the MFMA phase, ahead of its barrier.
+    advance(cur_v);
+    advance(cur_k);
     softmax_phase(true);
     phase_barrier();
   };
