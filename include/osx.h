@@ -203,7 +203,8 @@ int osx_softmax_rows_ex(const void* x, void* y, int dtype, int64_t rows, int64_t
  *                     and summed; then y multiplied by 1/sum.  Per-chunk
  *                     partials in the workspace instead of the page's single
  *                     256-thread block, so long rows use the whole GPU.
- * Each row is cut into 16384-element chunks, one workgroup per chunk.
+ * Each row is cut into chunks of 32768 (ATOMIC) or 16384 (STASH) elements, one
+ * workgroup per chunk.
  * Errors as osx_softmax_rows; an unknown method is OSX_EINVAL.
  */
 #define OSX_3PASS_ATOMIC 1

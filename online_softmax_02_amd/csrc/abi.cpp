@@ -303,7 +303,7 @@ int plan_3pass(int64_t rows, int64_t cols, int method, int* splits, int64_t* gri
   *ws = 0;
   if (rows == 0) return ok();
   if (cols == 0) return fail(OSX_EINVAL, "cols == 0 with rows > 0: softmax over nothing");
-  const int64_t sp = cdiv(cols, osx::kSoftmaxChunk);
+  const int64_t sp = cdiv(cols, osx::softmax_3pass_chunk(method));
   if (rows * sp > 0x7fffffff) return fail(OSX_EUNSUPPORTED, "problem needs %lld workgroups", (long long)(rows * sp));
   *splits = (int)sp;
   *grid = rows * sp;
@@ -435,7 +435,7 @@ int osx_softmax_rows_3pass(const float* x, float* y, int64_t rows, int64_t cols,
   a.cols = cols;
   a.method = method;
   a.splits = splits;
-  a.chunk = osx::kSoftmaxChunk;
+  a.chunk = osx::softmax_3pass_chunk(method);
   a.grid = grid;
   a.workspace = workspace;
   a.stream = (hipStream_t)stream;

@@ -26,7 +26,14 @@ constexpr int kSplitMinBlocks = 4;     // ... keeping at least this many key blo
 constexpr int kSoftmaxThreads = 256;
 constexpr int64_t kSoftmaxWaveMax = 2048;  // longest row held by one wavefront (32 elements per lane)
 constexpr int64_t kSoftmaxRowMax = 8192;   // longest row held by one workgroup (32 elements per thread)
-constexpr int64_t kSoftmaxChunk = 16384;   // elements per workgroup when a row is split
+constexpr int64_t kSoftmaxChunk = 32768;   // elements per workgroup when a row is split
+// Chunk lengths of the three-pass comparators, each the faster of 16384 and
+// 32768 for its own design on a 2^24-element row.
+constexpr int64_t kSoftmax3PassChunkAtomic = 32768;
+constexpr int64_t kSoftmax3PassChunkStash = 16384;
+constexpr int64_t softmax_3pass_chunk(int method) {
+  return method == OSX_3PASS_ATOMIC ? kSoftmax3PassChunkAtomic : kSoftmax3PassChunkStash;
+}
 
 struct AttnArgs {
   const void* q;

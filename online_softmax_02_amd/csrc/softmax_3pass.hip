@@ -13,7 +13,7 @@
 //   pass is spread over chunk workgroups, whose per-chunk partials (a max, then
 //   a sum) the next pass combines.
 //
-// fp32 in and out.  Rows are cut into kSoftmaxChunk-element chunks, one
+// fp32 in and out.  Rows are cut into chunks (softmax_3pass_chunk), one
 // workgroup each, as in the split two-pass kernels; 16-byte loads when the
 // row length is a multiple of 4 and x / y are 16-byte aligned.
 #include "common.hpp"

@@ -113,7 +113,7 @@ def test_plans_for_the_workloads():
     assert osx.softmax_rows_plan(3, 8192)["kernel_name"] == "softmax_row"
     assert osx.softmax_rows_plan(3, 8193)["kernel_name"] == "softmax_split"
     p = osx.softmax_rows_plan(1, 1 << 24)
-    assert p["kernel_name"] == "softmax_split" and p["splits"] == (1 << 24) // 16384
+    assert p["kernel_name"] == "softmax_split" and p["splits"] == (1 << 24) // p["block_m"]
     assert osx.softmax_rows_workspace(1, 1 << 24) == p["splits"] * 8
 
 
@@ -155,7 +155,7 @@ def test_softmax_3pass_workspace_and_rejects():
     lib = osx.lib
     A, S = osx.OSX_3PASS_ATOMIC, osx.OSX_3PASS_STASH
     assert osx.softmax_rows_3pass_workspace(3, 100, A) == 3 * 8            # (max, sum) per row
-    assert osx.softmax_rows_3pass_workspace(3, 40000, S) == 3 * 3 * 8      # (max, sum) per 16384-element chunk
+    assert osx.softmax_rows_3pass_workspace(3, 3 * 16384 + 17, S) == 3 * 4 * 8  # (max, sum) per 16384-element chunk
     assert osx.softmax_rows_3pass_workspace(0, 100, S) == 0
     x, y, ws = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x900000), ctypes.c_void_p(0x2000000)
     assert lib.osx_softmax_rows_3pass(x, y, 4, 16, 3, ws, 64, None) == osx.OSX_EINVAL     # method

@@ -176,7 +176,7 @@ def test_decode_mid_sizes(osx, case):
     check(got, oracle.attention(t["q"], t["k"], t["v"]), "bf16", f"decode {case}")
 
 
-SOFTMAX_CASES = [(1, 1), (3, 7), (5, 4), (2, 255), (1, 8192), (2, 8193), (3, 16384 * 2 + 5), (2, 100000),
+SOFTMAX_CASES = [(1, 1), (3, 7), (5, 4), (2, 255), (1, 8192), (2, 8193), (3, 16384 * 2 + 5), (2, 32768 * 2 + 5), (2, 100000),
                  (64, 1000), (1, 1 << 20)]
 
 

@@ -27,7 +27,7 @@ def osx():
 
 
 METHODS = {"atomic": 1, "stash": 2}
-SHAPES = [(4, 200), (3, 1001), (5, 40000), (2, 16384), (7, 3)]
+SHAPES = [(4, 200), (3, 1001), (5, 40000), (2, 16384), (2, 32768), (2, 32769), (2, 70001), (7, 3)]
 
 
 @pytest.mark.parametrize("method", list(METHODS))
@@ -43,7 +43,7 @@ def test_3pass_matches_oracle(osx, method, shape):
 
 @pytest.mark.parametrize("method", list(METHODS))
 def test_3pass_long_row_workload(osx, method):
-    """x[1, 2^24] with a +50 spike in the last 1%: 1024 chunks merge one (max, sum)."""
+    """x[1, 2^24] with a +50 spike in the last 1%: all the row's chunks merge one (max, sum)."""
     w = synth.WORKLOADS["softmax_1x16m"]
     x = synth.softmax_inputs(w)
     print(f"case 3pass {method} {w.name}", flush=True)

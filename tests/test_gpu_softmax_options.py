@@ -75,17 +75,25 @@ def test_softmax_options_match_oracle(osx, case):
 
 
 def test_softmax_options_large_masked_rows_sampled(osx):
-    """[16400, 16500] fp32, one causal head: rows are split into 2 chunks and their visible part ends in
-    chunk 0, exactly at the chunk edge, or in chunk 1; sampled rows against the oracle."""
-    rows, cols = 16400, 16500
-    x = _inputs("f32", rows, cols, 11)
-    y = osx.softmax_rows(to_dev(x), causal_period=rows)
+    """One causal fp32 head of [chunk + 40, chunk + 136] rows (chunk = the split kernels' chunk length, from the
+    plan): every row is split into 2 chunks, and the visible part of the sampled rows ends inside chunk 0,
+    exactly at its last column, at the first column of chunk 1, or inside chunk 1.  The 4.3 GB input is drawn
+    on the GPU (seeded torch generator); the sampled rows are copied back for the oracle."""
+    chunk = osx.softmax_rows_plan(1, 1 << 24)["block_m"]
+    rows, cols = chunk + 40, chunk + 136
+    assert osx.softmax_rows_plan(rows, cols)["kernel_name"] == "softmax_split"
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    xd = torch.randn(rows, cols, device="cuda", generator=gen).mul_(3.0)
+    y = osx.softmax_rows(xd, causal_period=rows)
     torch.cuda.synchronize()
-    pick = np.array([0, 1, 5000, 16382, 16383, 16384, 16385, 16399])
-    got = y[torch.from_numpy(pick).cuda()].cpu().numpy().astype(np.float64)
+    pick = np.array([0, 1, 5000, chunk - 2, chunk - 1, chunk, chunk + 1, rows - 1])
+    idx = torch.from_numpy(pick).cuda()
+    x = xd[idx].cpu().numpy()
+    got = y[idx].cpu().numpy().astype(np.float64)
+    del xd, y
     ref = np.zeros((len(pick), cols))
     for i, r in enumerate(pick):  # row r keeps columns <= r: the oracle on that row's visible prefix
-        ref[i, :r + 1] = oracle.softmax_rows(x[r:r + 1, :r + 1])[0]
+        ref[i, :r + 1] = oracle.softmax_rows(x[i:i + 1, :r + 1])[0]
     _check(got, ref, "f32", 0, "sampled rows")
     for i, r in enumerate(pick):
         assert (got[i, r + 1:] == 0).all()
