@@ -491,7 +491,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
   // for block g (V in stage P), loads of stage P+3 (V of block g+3, K of block
   // g+4).  Softmax phase: block g+1.
   auto block = [&](int P) __attribute__((always_inline)) {
-    __builtin_amdgcn_s_setprio(2);  // the MFMA phase wins issue slots over the other group's softmax
+    __builtin_amdgcn_s_setprio(3);  // the MFMA phase wins issue slots over the other group's softmax
     // Always the full MFMA phase: a block this wavefront cannot see has zero
     // weights (its PV adds nothing) and its scores go unused.
     gemm_fast(k_stage[P], v_stage[P], k_stage[(P + 3) % kStages], v_stage[(P + 3) % kStages]);
