@@ -18,6 +18,8 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+#include <type_traits>
+
 namespace osx {
 namespace {
 
@@ -30,11 +32,19 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 struct Head {
   int64_t q, kv;  // flat query head (b * Hq + h) and its KV head (b * Hkv + h / G)
+  int qb;         // 128-query block within the head
 };
 
+// Workgroup -> (query head, query block).  Workgroups are dealt to the 8 XCDs
+// round-robin in launch order; numbering them so that each XCD receives a
+// contiguous run of (head, block) pairs keeps the workgroups of one XCD on the
+// same few K or V heads (one L2 per XCD) and writing neighbouring rows.
 __device__ __forceinline__ Head head_of(int Hq, int Hkv) {
+  const int64_t gx = gridDim.x, total = gx * gridDim.y, L = blockIdx.y * gx + blockIdx.x;
+  const int64_t id = total % 8 == 0 ? (L % 8) * (total / 8) + L / 8 : L;
   Head h;
-  h.q = blockIdx.y;
+  h.q = id / gx;
+  h.qb = (int)(id - h.q * gx);
   const int64_t b = h.q / Hq;
   const int hq = (int)(h.q - b * Hq);
   h.kv = b * Hkv + hq / (Hq / Hkv);
@@ -46,74 +56,100 @@ __device__ __forceinline__ Head head_of(int Hq, int Hkv) {
 // 32w .. 32w + 31 of them.  Lane (i = lane % 32, hf = lane / 32) holds the B
 // operand Q[q0 + i][16 kc + 8 hf .. + 7] for every k-step kc, and per 32-key
 // block loads the A operand K[j0 + i][16 kc + 8 hf .. + 7]; the next block's
-// K is loaded while the current one is multiplied.  Rows past Sq or Sk load
-// as zero (buffer range check) and are not stored.  Each 32 x 32 tile goes
-// through the wavefront's own LDS tile, so that a store instruction writes 8
-// whole 128-byte row segments instead of 32-byte pieces of 32 rows.
+// K is loaded while the current one is multiplied.  kGroupBlocks blocks (a
+// 32 x 128 group of scores) accumulate in registers and then pass through the
+// wavefront's own LDS tile, so that each store instruction writes two whole
+// 512-byte row segments: long runs in each DRAM page rather than 128-byte
+// pieces of 32 rows.  Rows past Sq or Sk load as zero (buffer range check);
+// a store to a row past Sq or a column past Sk goes to an offset outside the
+// head's score matrix and is dropped.
+constexpr int kGroupBlocks = 4;
+constexpr int kNonTemporal = 2;               // buffer-op cache policy: S is streamed once
+constexpr uint32_t kOffNowhere = 0x80000000u;  // an offset past any head's scores (at most 2^31 bytes)
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void scores_bf16_kernel(const uint16_t* __restrict__ Q,
                                                                const uint16_t* __restrict__ K, float* __restrict__ S,
                                                                int Hq, int Hkv, int Sq, int Sk, float scale) {
   constexpr int KC = D / 16;
-  constexpr int kTileStride = 36;  // floats per LDS tile row: 32 keys + 4 of padding (16-byte aligned)
+  constexpr int NB = kGroupBlocks;
+  constexpr int GK = 32 * NB;           // keys per group
+  constexpr int kTileStride = GK + 4;   // floats per LDS tile row: 16-byte aligned, consecutive rows 4 banks apart
   __shared__ __attribute__((aligned(16))) float tiles[kThreads / 64][32 * kTileStride];
   const Head hd = head_of(Hq, Hkv);
   const int lane = threadIdx.x & 63, i = lane & 31, hf = lane >> 5;
-  const int q0 = blockIdx.x * kRowsPerWg + (threadIdx.x >> 6) * 32;
+  const int q0 = hd.qb * kRowsPerWg + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * 32;
   const int q = q0 + i;
   float* tile = tiles[threadIdx.x >> 6];
   const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q + hd.q * Sq * D, (uint32_t)Sq * D * 2);
   const __amdgpu_buffer_rsrc_t kr = make_rsrc(K + hd.kv * Sk * D, (uint32_t)Sk * D * 2);
-  float* Sh = S + hd.q * (int64_t)Sq * Sk;
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(S + hd.q * (int64_t)Sq * Sk, (uint32_t)((int64_t)Sq * Sk * 4));
   bf16x8 qf[KC];
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc)
     qf[kc] = __builtin_bit_cast(bf16x8, buf_ld16(qr, (uint32_t)(q * D + 16 * kc + 8 * hf) * 2));
-  const int nblk = (Sk + 31) / 32;
+  const int ngrp = (Sk + GK - 1) / GK;
   const bool vec = (Sk & 3) == 0;
   bf16x8 ka[KC], kb[KC];
+  // Loads past Sk (the last group's tail and the prefetch after it) return zeros.
   auto load_k = [&](int jb, bf16x8 (&dst)[KC]) {
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc)
       dst[kc] = __builtin_bit_cast(bf16x8, buf_ld16(kr, (uint32_t)((jb * 32 + i) * D + 16 * kc + 8 * hf) * 2));
   };
-  // Lane (r = 8 s + lane / 8, c = 4 (lane % 8)) writes keys c .. c + 3 of tile row r.
-  const int rd_row = lane >> 3, rd_col = 4 * (lane & 7);
-  auto block = [&](int jb, const bf16x8 (&kf)[KC]) {
+  auto mma = [&](const bf16x8 (&kf)[KC]) {
     f32x16 acc = f32x16{};
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kc], qf[kc], acc, 0, 0, 0);
-    // acc[4a + e] is S[q0 + i][jb * 32 + 8a + 4hf + e]: into tile row i.
+    return acc;
+  };
+  // Group g's tile to S.  Store s: the lanes of half hf write keys
+  // g GK + 4 i .. + 3 of tile row 2 s + hf, one 16-byte store each when rows are
+  // 16-byte aligned (Sk % 4 == 0), else four 4-byte stores.
+  auto store_group = [&](int g, const float* t, auto aligned) {
+    const int j = g * GK + 4 * i;
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
-      *reinterpret_cast<f32x4*>(tile + i * kTileStride + 8 * a + 4 * hf) =
-          f32x4{acc[4 * a] * scale, acc[4 * a + 1] * scale, acc[4 * a + 2] * scale, acc[4 * a + 3] * scale};
-    const int j = jb * 32 + rd_col;
-#pragma unroll
-    for (int s8 = 0; s8 < 4; ++s8) {
-      const int r = 8 * s8 + rd_row;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(tile + r * kTileStride + rd_col);
-      if (q0 + r >= Sq) continue;
-      float* row = Sh + (int64_t)(q0 + r) * Sk;
-      if (vec && j + 3 < Sk) {
-        *reinterpret_cast<f32x4*>(row + j) = v;
+    for (int s = 0; s < 16; ++s) {
+      const int r = 2 * s + hf;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(t + r * kTileStride + 4 * i);
+      const bool row_ok = q0 + r < Sq;
+      const uint32_t base = (uint32_t)(q0 + r) * (uint32_t)Sk + (uint32_t)j;  // < 2^29 where it is used
+      if constexpr (decltype(aligned)::value) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), sr,
+                                               row_ok && j < Sk ? 4u * base : kOffNowhere, 0, kNonTemporal);
       } else {
-        if (j < Sk) row[j] = v.x;
-        if (j + 1 < Sk) row[j + 1] = v.y;
-        if (j + 2 < Sk) row[j + 2] = v.z;
-        if (j + 3 < Sk) row[j + 3] = v.w;
+        const u32x4 w = __builtin_bit_cast(u32x4, v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          __builtin_amdgcn_raw_buffer_store_b32(w[e], sr, row_ok && j + e < Sk ? 4u * (base + e) : kOffNowhere, 0,
+                                                kNonTemporal);
       }
     }
   };
-  // Two register sets for K: block jb + 1 loads while block jb is multiplied.
   load_k(0, ka);
-  for (int jb = 0; jb < nblk; jb += 2) {
-    if (jb + 1 < nblk) load_k(jb + 1, kb);
-    block(jb, ka);
-    if (jb + 1 < nblk) {
-      if (jb + 2 < nblk) load_k(jb + 2, ka);
-      block(jb + 1, kb);
+  for (int g = 0; g < ngrp; ++g) {
+    // Two register sets for K: block jb + 1 loads while block jb is multiplied.
+    f32x16 acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; b += 2) {
+      const int jb = g * NB + b;
+      load_k(jb + 1, kb);
+      acc[b] = mma(ka);
+      load_k(jb + 2, ka);
+      acc[b + 1] = mma(kb);
     }
+    // acc[b][4a + e] is S[q0 + i][g GK + 32 b + 8 a + 4 hf + e]: into tile row i.
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        *reinterpret_cast<f32x4*>(tile + i * kTileStride + 32 * b + 8 * a + 4 * hf) =
+            f32x4{acc[b][4 * a] * scale, acc[b][4 * a + 1] * scale, acc[b][4 * a + 2] * scale,
+                  acc[b][4 * a + 3] * scale};
+    if (vec)
+      store_group(g, tile, std::true_type{});
+    else
+      store_group(g, tile, std::false_type{});
   }
 }
 
@@ -151,7 +187,7 @@ __global__ __launch_bounds__(kThreads) void pv_bf16_kernel(const float* __restri
   __shared__ __attribute__((aligned(16))) unsigned char lds_v[2][T::BLOCK_BYTES];
   const Head hd = head_of(Hq, Hkv);
   const int lane = threadIdx.x & 63, i = lane & 31, hf = lane >> 5;
-  const int q = blockIdx.x * kRowsPerWg + (threadIdx.x >> 6) * 32 + i;
+  const int q = hd.qb * kRowsPerWg + (threadIdx.x >> 6) * 32 + i;
   const __amdgpu_buffer_rsrc_t pr = make_rsrc(P + hd.q * (int64_t)Sq * Sk, (uint32_t)((int64_t)Sq * Sk * 4));
   const __amdgpu_buffer_rsrc_t vr = make_rsrc(V + hd.kv * Sk * D, (uint32_t)Sk * D * 2);
   const int nblk = (Sk + kKeyBlock - 1) / kKeyBlock;
