@@ -18,7 +18,9 @@ softmax_rows     the stable row softmax (page "Softmax 算子的实现与优化"
                  max-shifted definition; page "Puzzle 8: Long Softmax", its spec).
 recurrence       a blockwise model of the online recurrence (running max, running
                  denominator, unnormalised accumulator) used to check page-fixed
-                 facts against the definition; it is not the oracle.
+                 facts against the definition; and ``attention_normalised``, the
+                 per-key normalised-output recurrence of page "Puzzle 9: Simple
+                 FlashAttention" (oracle of the normalised-output variant).
 brute            pure-Python loops over tiny inputs.
 
 Every function is pinned by ``tests/test_oracle_pins.py`` to values, closed

@@ -9,6 +9,11 @@ blocks, state = running max m, denominator l, accumulator acc; each block
 rescales the history by exp(m_old - m_new)) and page "Softmax 算子的实现与优化",
 section Online Softmax (the boxed update m' = max(m, m_b),
 l' = l e^{m - m'} + sum_{x in B} e^{x - m'}, started from m = -inf, l = 0).
+
+``attention_normalised`` is the other recurrence of page "Puzzle 9: Simple
+FlashAttention", which keeps the output normalised at every key; it is the
+oracle for the library's normalised-output attention variant, pinned to the
+plain definition and to prefix softmaxes.
 """
 import math
 
@@ -88,3 +93,51 @@ def attention_blockwise(q, k, v, *, scale=None, block: int = 32, tail: str = "ne
         out[i] = acc / l
         traces.append(hist)
     return (out, traces) if trace else out
+
+
+def attention_normalised(q, k, v, *, scale=None, causal: bool = False, trace_row: int | None = None):
+    """Single-head attention via the normalised-output recurrence, one key at a time.
+
+    Page "Puzzle 9: Simple FlashAttention" (fadingcoder.top), the recurrence
+    under its scalar FlashAttention spec: for each query row and each key i in
+    order, with x_i the scaled score,
+        m_i  = max(m_{i-1}, x_i)
+        d'_i = d'_{i-1} e^{m_{i-1} - m_i} + e^{x_i - m_i}
+        O'_i = O'_{i-1} (d'_{i-1} / d'_i) e^{m_{i-1} - m_i} + (e^{x_i - m_i} / d'_i) V_i
+    started from m_0 = -inf, d'_0 = 0, O'_0 = 0.  O' stays normalised at every
+    step, so the last O' is the output with no final division.  Keys a row
+    may not see (causal, query index < key index, with more than one query
+    row) are skipped: a score of -inf would leave m, d' and O' unchanged.
+
+    q: [M, D], k, v: [N, D].  Returns (O [M, D], m [M], d' [M]) with m the
+    natural-log-domain running max.  With ``trace_row`` also returns the list
+    of O'_i of that row after every visible key.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    M, D = q.shape
+    N = k.shape[0]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out = np.zeros((M, D))
+    m_out = np.full(M, -math.inf)
+    d_out = np.zeros(M)
+    hist = []
+    for r in range(M):
+        m, d, o = -math.inf, 0.0, np.zeros(D)
+        last = r if (causal and M > 1) else N - 1
+        for i in range(min(last, N - 1) + 1):
+            x = float(q[r] @ k[i]) * scale
+            m_new = max(m, x)
+            shrink = math.exp(m - m_new)  # e^{m_{i-1} - m_i}; 0 on the first key
+            e = math.exp(x - m_new)
+            d_new = d * shrink + e
+            o = o * (d / d_new) * shrink + (e / d_new) * v[i]
+            m, d = m_new, d_new
+            if r == trace_row:
+                hist.append(o.copy())
+        out[r], m_out[r], d_out[r] = o, m, d
+    if trace_row is not None:
+        return out, m_out, d_out, hist
+    return out, m_out, d_out

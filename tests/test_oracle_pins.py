@@ -336,3 +336,72 @@ def test_softmax_masked_brute_force_and_bf16_decoding():
     bits = np.array([[0x3F80, 0x4000, 0xC040]], dtype=np.uint16)  # 1, 2, -3 in bf16
     np.testing.assert_allclose(oracle.softmax_rows(bits), oracle.softmax_rows(np.array([[1.0, 2.0, -3.0]])),
                                rtol=1e-15)
+
+
+# ---------------------------------------------------------------- normalised-output recurrence
+def test_normalised_recurrence_matches_definition():
+    """Page "Puzzle 9: Simple FlashAttention": the normalised recurrence ends at softmax(x) V, no final division."""
+    for causal in (False, True):
+        M, N, D = (9, 9, 5) if causal else (7, 40, 5)
+        q = RNG.standard_normal((M, D)) * 2.0
+        k = RNG.standard_normal((N, D))
+        v = RNG.standard_normal((N, D))
+        o, _, _ = recurrence.attention_normalised(q, k, v, causal=causal)
+        ref = oracle.attention(q[None, None], k[None, None], v[None, None], causal=causal)[0, 0]
+        np.testing.assert_allclose(o, ref, rtol=1e-12, atol=1e-13)
+        want = np.array(brute.attention(q[None, None].tolist(), k[None, None].tolist(), v[None, None].tolist(),
+                                        causal=causal))[0, 0]
+        np.testing.assert_allclose(o, want, rtol=1e-12, atol=1e-13)
+
+
+def test_normalised_output_is_the_prefix_softmax_after_every_key():
+    """O'_i is the attention output over keys 1..i at every step (the invariant that makes O' normalised)."""
+    D = 4
+    q = RNG.standard_normal((3, D))
+    k = RNG.standard_normal((25, D))
+    k[11] *= 6.0  # a late key that moves the running max by a lot
+    v = RNG.standard_normal((25, D))
+    scale = 0.7
+    _, _, _, hist = recurrence.attention_normalised(q, k, v, scale=scale, trace_row=1)
+    x = (k @ q[1]) * scale
+    assert len(hist) == 25
+    for i, o_i in enumerate(hist):
+        w = scipy.special.softmax(x[: i + 1])
+        np.testing.assert_allclose(o_i, w @ v[: i + 1], rtol=1e-12, atol=1e-13)
+
+
+def test_normalised_state_is_max_and_denominator():
+    """The final (m, d') are max_j x_j and sum_j e^{x_j - m}: m + log d' is the row's log-sum-exp."""
+    q = RNG.standard_normal((6, 3))
+    k = RNG.standard_normal((30, 3))
+    v = RNG.standard_normal((30, 3))
+    for causal in (False, True):
+        kk = k[:6] if causal else k
+        vv = v[:6] if causal else v
+        _, m, d = recurrence.attention_normalised(q, kk, vv, causal=causal)
+        s = (q @ kk.T) / math.sqrt(3)
+        if causal:
+            s = np.where(np.tril(np.ones((6, 6), dtype=bool)), s, -np.inf)
+        np.testing.assert_allclose(m, s.max(axis=1), rtol=1e-15)
+        np.testing.assert_allclose(d, np.exp(s - s.max(axis=1, keepdims=True)).sum(axis=1), rtol=1e-13)
+        lse = oracle.attention_lse(q[None, None], kk[None, None], causal=causal)[0, 0]
+        np.testing.assert_allclose(m + np.log(d), lse, rtol=1e-13, atol=1e-13)
+
+
+def test_normalised_two_keys_closed_form():
+    """Two keys, d = 1: O = v1 sigma(x1 - x2) + v2 sigma(x2 - x1), also when the second key jumps the max by 50."""
+    for x1, x2 in ((0.3, -1.2), (0.0, 50.0), (-7.0, -7.0)):
+        q = np.array([[1.0]])
+        k = np.array([[x1], [x2]])
+        v = np.array([[2.0], [-3.0]])
+        o, m, d = recurrence.attention_normalised(q, k, v, scale=1.0)
+        s1 = scipy.special.expit(x1 - x2)
+        assert o[0, 0] == pytest.approx(2.0 * s1 - 3.0 * (1.0 - s1), rel=1e-14, abs=1e-15)
+        assert m[0] == max(x1, x2)
+        assert d[0] == pytest.approx(1.0 + math.exp(min(x1, x2) - max(x1, x2)), rel=1e-15)
+    # causal first row sees key 0 only: its output is V[0] exactly
+    q = RNG.standard_normal((4, 3))
+    k = RNG.standard_normal((4, 3))
+    v = RNG.standard_normal((4, 3))
+    o, _, _ = recurrence.attention_normalised(q, k, v, causal=True)
+    assert np.array_equal(o[0], v[0])
