@@ -254,6 +254,30 @@ def bench_f32(torch, osx, args):
             "roofline": roofline("mfma", tf, PEAK_F32_TFLOPS, "TFLOP/s", traffic_for("prefill_f32_kernel"))}
 
 
+def bench_f32_normalised(torch, osx, args, plain_us):
+    """The normalised-output recurrence (O kept normalised after every block) on the same fp32 workload."""
+    import synth
+    w = synth.WORKLOADS["attn_f32_4k_d128"]
+    _, q, k, v = attn_tensors(torch, w)
+    out = torch.empty_like(q)
+    wall, ms = timed(torch, lambda i: osx.attn_fwd_normalised(q, k, v, out=out), args.steps, args.warmup)
+    tf = w.flops() / (ms * 1e-3) / 1e12
+    return {"workload": w.name, "unit": "TFLOP/s", "value": round(tf, 2), "call_us": round(ms * 1e3, 2),
+            "time_vs_unnormalised": round(ms * 1e3 / plain_us, 3),
+            "roofline": roofline("mfma", tf, PEAK_F32_TFLOPS, "TFLOP/s", None)}
+
+
+def bench_lse(torch, osx, args, q, k, v, w, plain_ms):
+    """The prefill call that also writes each query row's log-sum-exp (osx_attn_fwd_lse)."""
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    wall, ms = timed(torch, lambda i: osx.attn_fwd(q, k, v, causal=True, out=out, lse=lse), args.steps, args.warmup)
+    tf = w.flops() / (ms * 1e-3) / 1e12
+    return {"workload": w.name, "unit": "TFLOP/s", "value": round(tf, 2), "call_us": round(ms * 1e3, 2),
+            "time_vs_without_lse": round(ms / plain_ms, 3),
+            "roofline": roofline("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s", None)}
+
+
 def bench_small(torch, osx, args):
     import synth
     res = {}
@@ -333,6 +357,8 @@ def main():
         return
     if args.only in ("f32",):
         also["attn_f32_4k_d128"] = bench_f32(torch, osx, args)
+        also["attn_f32_normalised_4k_d128"] = bench_f32_normalised(torch, osx, args,
+                                                                   also["attn_f32_4k_d128"]["call_us"])
         print(json.dumps({"also": also}))
         return
     if args.only in ("small",):
@@ -341,12 +367,14 @@ def main():
 
     head, t, w = bench_prefill(torch, osx, args)
     log(f"[bench] prefill {head['tflops']:.1f} TFLOP/s ({head['kernel_ms']:.3f} ms per call)")
+    qkv = head.pop("qkv")
     if args.only in ("all", "unfused"):
-        also["attn_unfused_gqa_prefill_bf16"] = bench_unfused(torch, osx, args, *head.pop("qkv"), w,
-                                                              head["kernel_ms"])
+        also["attn_unfused_gqa_prefill_bf16"] = bench_unfused(torch, osx, args, *qkv, w, head["kernel_ms"])
         log(f"[bench] unfused comparator {also['attn_unfused_gqa_prefill_bf16']['call_us']} us")
-    else:
-        head.pop("qkv")
+    if args.only == "all":
+        also["attn_lse_gqa_prefill_bf16"] = bench_lse(torch, osx, args, *qkv, w, head["kernel_ms"])
+        log(f"[bench] prefill with lse {also['attn_lse_gqa_prefill_bf16']['value']} TFLOP/s")
+    del qkv
     if args.only == "unfused":
         print(json.dumps({"also": also}))
         return
@@ -361,6 +389,9 @@ def main():
         log("[bench] three-pass comparators done")
         also["attn_f32_4k_d128"] = bench_f32(torch, osx, args)
         log(f"[bench] fp32 attention {also['attn_f32_4k_d128']['value']} TFLOP/s")
+        also["attn_f32_normalised_4k_d128"] = bench_f32_normalised(torch, osx, args,
+                                                                   also["attn_f32_4k_d128"]["call_us"])
+        log(f"[bench] fp32 normalised-output attention {also['attn_f32_normalised_4k_d128']['value']} TFLOP/s")
         also.update(bench_small(torch, osx, args))
     cpu = None
     if not args.no_cpu_baseline and args.only == "all":

@@ -124,6 +124,29 @@ int osx_attn_fwd_lse(const void* q, const void* k, const void* v, void* o, float
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * osx_attn_fwd_normalised -- the same O as osx_attn_fwd, computed with the
+ * normalised-output form of the recurrence (page "Puzzle 9: Simple
+ * FlashAttention", the recurrence under its scalar FlashAttention spec):
+ *     m_i  = max(m_{i-1}, x_i)
+ *     d'_i = d'_{i-1} e^{m_{i-1} - m_i} + e^{x_i - m_i}
+ *     O'_i = O'_{i-1} (d'_{i-1} / d'_i) e^{m_{i-1} - m_i} + (e^{x_i - m_i} / d'_i) V_i
+ * applied per block of 32 keys, so the accumulator holds the normalised output
+ * after every block and the epilogue divides by nothing.  When the keys are
+ * split across workgroups (the same plan as osx_attn_fwd), the slices'
+ * normalised outputs are merged with weights d'_s e^{m_s - m} / sum.
+ *
+ * fp32 only: dtype OSX_BF16 returns OSX_EUNSUPPORTED (the bf16 kernels sum
+ * the denominator on the matrix cores after the P V product, which this form
+ * needs before it).  lse: NULL, or a device pointer to batch * heads_q * seq_q
+ * fp32 values written as by osx_attn_fwd_lse.  The workspace is the size
+ * osx_attn_fwd_workspace reports for the same fp32 problem.  Everything else,
+ * errors included, as osx_attn_fwd.
+ */
+int osx_attn_fwd_normalised(const void* q, const void* k, const void* v, void* o, float* lse, int dtype, int batch,
+                            int heads_q, int heads_kv, int seq_q, int seq_k, int head_dim, int causal, float scale,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * osx_attn_fwd_unfused -- the same O as osx_attn_fwd, computed the unfused way
  * as a comparator: the three kernels of page "从零开始写Qwen3（五-其一）使用Triton
  * 实现自注意力" (sections 免转置矩阵乘法, softmax的triton实现, 串起来):

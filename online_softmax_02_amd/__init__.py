@@ -58,6 +58,7 @@ def _load() -> ctypes.CDLL:
     lib.osx_attn_fwd_workspace.argtypes = attn_shape + [ctypes.POINTER(_sz)]
     lib.osx_attn_fwd.argtypes = [_vp, _vp, _vp, _vp] + attn_shape + [_f, _vp, _sz, _vp]
     lib.osx_attn_fwd_lse.argtypes = [_vp, _vp, _vp, _vp, _vp] + attn_shape + [_f, _vp, _sz, _vp]
+    lib.osx_attn_fwd_normalised.argtypes = [_vp, _vp, _vp, _vp, _vp] + attn_shape + [_f, _vp, _sz, _vp]
     lib.osx_softmax_rows_plan.argtypes = [_i64, _i64, ctypes.POINTER(Plan)]
     lib.osx_softmax_rows_workspace.argtypes = [_i64, _i64, ctypes.POINTER(_sz)]
     lib.osx_softmax_rows.argtypes = [_vp, _vp, _i64, _i64, _vp, _sz, _vp]
@@ -71,7 +72,8 @@ def _load() -> ctypes.CDLL:
     lib.osx_last_error.argtypes = []
     lib.osx_last_error.restype = ctypes.c_char_p
     lib.osx_version.argtypes = []
-    for name in ("osx_attn_plan", "osx_attn_fwd_workspace", "osx_attn_fwd", "osx_attn_fwd_lse", "osx_softmax_rows_plan",
+    for name in ("osx_attn_plan", "osx_attn_fwd_workspace", "osx_attn_fwd", "osx_attn_fwd_lse",
+                 "osx_attn_fwd_normalised", "osx_softmax_rows_plan",
                  "osx_softmax_rows_workspace", "osx_softmax_rows", "osx_softmax_rows_ex",
                  "osx_softmax_rows_3pass_workspace", "osx_softmax_rows_3pass", "osx_attn_fwd_unfused_workspace",
                  "osx_attn_fwd_unfused", "osx_version"):
@@ -148,16 +150,8 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}: float32 or bfloat16")
 
 
-def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, workspace=None, stream=None,
-             return_lse: bool = False, lse=None):
-    """O = softmax(mask(q k^T * scale)) v on the GPU.
-
-    q: [B, Hq, Sq, D] (or [M, D] for one head), k, v: [B, Hkv, Sk, D] (or
-    [N, D]); contiguous CUDA tensors of one dtype (float32 or bfloat16).
-    Query head h reads KV head h // (Hq // Hkv).  Returns a tensor like q; with
-    ``return_lse`` also the float32 [B, Hq, Sq] (or [M]) log-sum-exp of each
-    row's scaled, masked scores (``lse`` may supply that tensor).
-    """
+def _attn_prepare(q, k, v, causal, out, workspace):
+    """Checks q, k, v and out, allocates what is missing; returns the 4-D views and the call arguments."""
     torch = _torch()
     squeeze = q.dim() == 2
     if squeeze:
@@ -185,20 +179,58 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return squeeze, q, k, v, out, code, (B, Hq, Hkv, Sq, Sk, D), ws_ptr, ws_len
+
+
+def _lse_tensor(q, shape, lse):
+    torch = _torch()
+    B, Hq, Sq = shape[0], shape[1], shape[3]
+    if lse is None:
+        return torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if lse.numel() != B * Hq * Sq or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor of B * Hq * Sq elements")
+    return lse
+
+
+def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, workspace=None, stream=None,
+             return_lse: bool = False, lse=None):
+    """O = softmax(mask(q k^T * scale)) v on the GPU.
+
+    q: [B, Hq, Sq, D] (or [M, D] for one head), k, v: [B, Hkv, Sk, D] (or
+    [N, D]); contiguous CUDA tensors of one dtype (float32 or bfloat16).
+    Query head h reads KV head h // (Hq // Hkv).  Returns a tensor like q; with
+    ``return_lse`` also the float32 [B, Hq, Sq] (or [M]) log-sum-exp of each
+    row's scaled, masked scores (``lse`` may supply that tensor).
+    """
+    squeeze, q, k, v, out, code, shape, ws_ptr, ws_len = _attn_prepare(q, k, v, causal, out, workspace)
     sc = float(scale) if scale else 0.0
     if not (return_lse or lse is not None):
-        _check(lib.osx_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), code, B, Hq, Hkv, Sq, Sk, D,
-                                int(causal), sc, ws_ptr, ws_len, _stream(q, stream)))
+        _check(lib.osx_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), code, *shape, int(causal),
+                                sc, ws_ptr, ws_len, _stream(q, stream)))
         return out[0, 0] if squeeze else out
-    if lse is None:
-        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
-    elif lse.numel() != B * Hq * Sq or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 tensor of B * Hq * Sq elements")
-    _check(lib.osx_attn_fwd_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), code, B, Hq,
-                                Hkv, Sq, Sk, D, int(causal), sc, ws_ptr, ws_len, _stream(q, stream)))
+    lse = _lse_tensor(q, shape, lse)
+    _check(lib.osx_attn_fwd_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), code, *shape,
+                                int(causal), sc, ws_ptr, ws_len, _stream(q, stream)))
     if squeeze:
         return out[0, 0], lse.reshape(-1)
     return out, lse
+
+
+def attn_fwd_normalised(q, k, v, causal: bool = False, scale: float | None = None, out=None, workspace=None,
+                        stream=None, return_lse: bool = False, lse=None):
+    """attn_fwd computed with the normalised-output recurrence (osx_attn_fwd_normalised): float32 only."""
+    squeeze, q, k, v, out, code, shape, ws_ptr, ws_len = _attn_prepare(q, k, v, causal, out, workspace)
+    sc = float(scale) if scale else 0.0
+    want = return_lse or lse is not None
+    if want:
+        lse = _lse_tensor(q, shape, lse)
+    _check(lib.osx_attn_fwd_normalised(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                       lse.data_ptr() if want else None, code, *shape, int(causal), sc, ws_ptr, ws_len,
+                                       _stream(q, stream)))
+    o = out[0, 0] if squeeze else out
+    if not want:
+        return o
+    return o, (lse.reshape(-1) if squeeze else lse)
 
 
 def softmax_rows(x, out=None, workspace=None, stream=None, causal_period: int = 0, scale: float = 1.0):
@@ -305,4 +337,4 @@ def softmax_rows_3pass(x, method: int, out=None, workspace=None, stream=None):
 __all__ = ["attn_fwd", "softmax_rows", "attn_plan", "attn_fwd_workspace", "softmax_rows_plan",
            "softmax_rows_workspace", "status_string", "last_error", "version", "OsxError", "lib", "LIB_PATH",
            "OSX_F32", "OSX_BF16", "softmax_rows_3pass", "softmax_rows_3pass_workspace", "OSX_3PASS_ATOMIC",
-           "OSX_3PASS_STASH", "attn_fwd_unfused", "attn_fwd_unfused_workspace"]
+           "OSX_3PASS_STASH", "attn_fwd_unfused", "attn_fwd_unfused_workspace", "attn_fwd_normalised"]

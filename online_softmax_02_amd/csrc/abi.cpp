@@ -170,10 +170,12 @@ namespace {
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, bool want_lse, int dtype, int batch,
              int heads_q, int heads_kv, int seq_q, int seq_k, int head_dim, int causal, float scale, void* workspace,
-             size_t workspace_bytes, void* stream) {
+             size_t workspace_bytes, void* stream, bool normalised = false) {
   osx_plan p;
   int st = plan_attn(dtype, batch, heads_q, heads_kv, seq_q, seq_k, head_dim, causal, &p);
   if (st != OSX_OK) return st;
+  if (normalised && dtype != OSX_F32)
+    return fail(OSX_EUNSUPPORTED, "the normalised-output recurrence is built for fp32 q, k, v and o only");
   if (p.kernel == OSX_KERNEL_NONE) return ok();
   if (!q || !k || !v || !o) return fail(OSX_EINVAL, "null q, k, v or o pointer");
   if (want_lse && !lse) return fail(OSX_EINVAL, "null lse pointer");
@@ -210,6 +212,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, b
   a.lse = lse;
   a.stream = (hipStream_t)stream;
   a.plan = p;
+  a.normalised = normalised ? 1 : 0;
   hipError_t e;
   switch (p.kernel) {
     case OSX_KERNEL_PREFILL_BF16: e = osx::launch_prefill_bf16(a); break;
@@ -238,6 +241,13 @@ int osx_attn_fwd_lse(const void* q, const void* k, const void* v, void* o, float
                      void* workspace, size_t workspace_bytes, void* stream) {
   return attn_fwd(q, k, v, o, lse, true, dtype, batch, heads_q, heads_kv, seq_q, seq_k, head_dim, causal, scale,
                   workspace, workspace_bytes, stream);
+}
+
+int osx_attn_fwd_normalised(const void* q, const void* k, const void* v, void* o, float* lse, int dtype, int batch,
+                            int heads_q, int heads_kv, int seq_q, int seq_k, int head_dim, int causal, float scale,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_fwd(q, k, v, o, lse, false, dtype, batch, heads_q, heads_kv, seq_q, seq_k, head_dim, causal, scale,
+                  workspace, workspace_bytes, stream, true);
 }
 
 int osx_softmax_rows_plan(int64_t rows, int64_t cols, osx_plan* out) {

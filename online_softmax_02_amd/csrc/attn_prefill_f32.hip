@@ -13,6 +13,15 @@
 // dimension d (a multiple of 4, at most 128) is padded with zeros up to DP,
 // a multiple of 32; padded columns are never stored.  Blocks are 32 keys.
 //
+// With NORM the kernel runs the normalised-output form of the recurrence
+// (page "Puzzle 9: Simple FlashAttention", the recurrence under its scalar
+// FlashAttention spec), applied per block of keys: the denominator d' of the
+// keys seen so far is complete after each block's exponentials, the
+// accumulator is multiplied by (d'_old / d'_new) 2^(m_old - m_new) and the
+// block's weights by 1 / d'_new before the P V product, so the accumulator is
+// the normalised output at every step and needs no final division.  Over one
+// block this is the per-key recurrence composed across the block's keys.
+//
 // Few heads with long sequences (one 4096-row head gives 32 workgroups) would
 // leave most of the 256 CUs idle, so the keys can be split: workgroup
 // (tile, split) runs the recurrence over its slice of the keys and writes the
@@ -45,7 +54,7 @@ __device__ __forceinline__ int k_swz(int row) {
   return CH % 16 == 0 ? (row & 15) : ((row >> 1) & 7);
 }
 
-template <int DP>
+template <int DP, bool NORM>
 __global__ __launch_bounds__(kAttnThreads, 2) void prefill_f32_kernel(
     const float* __restrict__ Qg, const float* __restrict__ Kg, const float* __restrict__ Vg, float* __restrict__ Og,
     float* __restrict__ Lse, int Hq, int Hkv, int Sq, int Sk, int d, int causal, float c, int hp, int n_hgroups,
@@ -205,12 +214,26 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_f32_kernel(
         s[r] = p;
         rsum += p;
       }
-      l_run = l_run * alpha + rsum;
-      m_run = m_new;
-      if (__ballot(alpha != 1.0f)) {
+      if constexpr (NORM) {
+        // d'_new = d'_old 2^(m_old - m_new) + the block's sum over both halves
+        // of the row (l_run holds the whole row's d' in both halves).  A row
+        // with nothing visible yet keeps d' = 0 and an all-zero accumulator.
+        const float d_new = l_run * alpha + (rsum + __shfl_xor(rsum, 32, 64));
+        const float inv_d = d_new > 0.f ? 1.0f / d_new : 0.f;
+        const float beta = l_run * alpha * inv_d;  // (d'_old / d'_new) 2^(m_old - m_new)
 #pragma unroll
-        for (int i = 0; i < T::DT; ++i) acc[i] *= alpha;
+        for (int i = 0; i < T::DT; ++i) acc[i] *= beta;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] *= inv_d;
+        l_run = d_new;
+      } else {
+        l_run = l_run * alpha + rsum;
+        if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+          for (int i = 0; i < T::DT; ++i) acc[i] *= alpha;
+        }
       }
+      m_run = m_new;
 
       // O^T += V^T P^T: lane (d, hf) reads V[key(r, hf)][d]
 #pragma unroll
@@ -229,12 +252,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_f32_kernel(
     __syncthreads();
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float l_tot = NORM ? l_run : l_run + __shfl_xor(l_run, 32, 64);
   if (q < Sq) {
     if (splits == 1) {
       // log sum_j exp(scale * s_j) = ln 2 * (m + log2 l), m in the log2 domain
       if (Lse && hf == 0) Lse[row_id] = (m_run + log2f(l_tot)) * kLn2;
-      const float inv = 1.0f / l_tot;
+      const float inv = NORM ? 1.0f : 1.0f / l_tot;
       float* op = Og + q_base + (size_t)q * d;
 #pragma unroll
       for (int dt = 0; dt < T::DT; ++dt)
@@ -248,7 +271,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_f32_kernel(
           }
         }
     } else {
-      // partial state of this slice: m (log2 domain), l and the unnormalised acc
+      // partial state of this slice: m (log2 domain), l and acc (unnormalised,
+      // or with NORM the slice's normalised output)
       if (hf == 0) {
         ws_ml[(row_id * splits + split) * 2] = m_run;
         ws_ml[(row_id * splits + split) * 2 + 1] = l_tot;
@@ -270,6 +294,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_f32_kernel(
 // Merge the key slices of each query row: one wavefront per row.  Lane s
 // (< splits <= 64) loads slice s's (m, l); the wavefront max and the weights
 // 2^(m_s - m) are shared by shuffles; lane c owns output columns c and c + 64.
+// With NORM the slices hold normalised outputs O'_s, weighted by
+// l_s 2^(m_s - m): O = sum_s l_s 2^(m_s - m) O'_s / l.
+template <bool NORM>
 __global__ __launch_bounds__(256) void combine_f32_kernel(const float* __restrict__ ws_ml,
                                                           const float* __restrict__ ws_acc, float* __restrict__ Og,
                                                           float* __restrict__ Lse, int64_t rows, int splits, int d) {
@@ -280,8 +307,9 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(const float* __restric
   const float m_s = lane < splits ? ml[2 * lane] : kNegInf;
   const float l_s = lane < splits ? ml[2 * lane + 1] : 0.f;
   const float M = wave_max(m_s);
-  const float w_s = lane < splits ? exp2_fast(m_s - M) : 0.f;  // 0 for an empty slice
-  const float L = wave_sum(l_s * w_s);
+  const float e_s = lane < splits ? exp2_fast(m_s - M) : 0.f;  // 0 for an empty slice
+  const float L = wave_sum(l_s * e_s);
+  const float w_s = NORM ? l_s * e_s : e_s;
   const float* pa = ws_acc + row * splits * d;
   float a0 = 0.f, a1 = 0.f;
   // Eight slices' partial outputs are loaded before any is used, so their load
@@ -321,13 +349,15 @@ hipError_t launch(const AttnArgs& a) {
   const int64_t rows = (int64_t)a.batch * a.heads_q * a.seq_q;
   float* ws_ml = static_cast<float*>(a.workspace);
   float* ws_acc = splits == 1 ? nullptr : ws_ml + rows * splits * 2;
-  hipLaunchKernelGGL(prefill_f32_kernel<DP>, dim3((unsigned)a.plan.grid), dim3(kAttnThreads), 0, a.stream,
+  auto kernel = a.normalised ? prefill_f32_kernel<DP, true> : prefill_f32_kernel<DP, false>;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)a.plan.grid), dim3(kAttnThreads), 0, a.stream,
                      static_cast<const float*>(a.q), static_cast<const float*>(a.k), static_cast<const float*>(a.v),
                      static_cast<float*>(a.o), a.lse, a.heads_q, a.heads_kv, a.seq_q, a.seq_k, a.head_dim, a.causal,
                      a.c, hp, n_hgroups, n_qtiles, units_per_tile, splits, kps, ws_ml, ws_acc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
-  hipLaunchKernelGGL(combine_f32_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, a.stream, ws_ml, ws_acc,
+  auto combine = a.normalised ? combine_f32_kernel<true> : combine_f32_kernel<false>;
+  hipLaunchKernelGGL(combine, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, a.stream, ws_ml, ws_acc,
                      static_cast<float*>(a.o), a.lse, rows, splits, a.head_dim);
   return hipGetLastError();
 }

@@ -46,6 +46,7 @@ struct AttnArgs {
   float* lse;  // optional: natural-log sum of exp(scaled, masked scores) per query row, or null
   hipStream_t stream;
   osx_plan plan;
+  int normalised = 0;  // fp32 only: run the normalised-output form of the recurrence
 };
 
 struct SoftmaxArgs {

@@ -137,6 +137,30 @@ def test_attn_fwd_lse_rejects_before_launch():
     assert lib.osx_attn_fwd_lse(None, None, None, None, None, BF16, 0, 4, 1, 16, 16, 128, 1, 0.0, None, 0, None) == 0
 
 
+def test_attn_fwd_normalised_rejects_before_launch():
+    lib = osx.lib
+    a, b, c, o = (ctypes.c_void_p(x) for x in (0x100000, 0x200000, 0x300000, 0x400000))
+    # the normalised-output form is built for fp32 only, even when there is no work
+    st = lib.osx_attn_fwd_normalised(a, b, c, o, None, BF16, 1, 4, 1, 16, 16, 128, 0, 0.0, None, 0, None)
+    assert st == osx.OSX_EUNSUPPORTED and "fp32" in osx.last_error()
+    st = lib.osx_attn_fwd_normalised(None, None, None, None, None, BF16, 0, 4, 1, 16, 16, 128, 0, 0.0, None, 0, None)
+    assert st == osx.OSX_EUNSUPPORTED
+    st = lib.osx_attn_fwd_normalised(None, None, None, None, None, F32, 1, 1, 1, 16, 16, 64, 0, 0.0, None, 0, None)
+    assert st == osx.OSX_EINVAL and "null" in osx.last_error()
+    # one 4096-row head splits its keys: the partials need the same workspace as osx_attn_fwd
+    need = osx.attn_fwd_workspace(F32, 1, 1, 1, 4096, 4096, 128)
+    assert need > 0
+    st = lib.osx_attn_fwd_normalised(a, b, c, ctypes.c_void_p(0x10000000), None, F32, 1, 1, 1, 4096, 4096, 128, 0,
+                                     0.0, ctypes.c_void_p(0x20000000), need - 1, None)
+    assert st == osx.OSX_EWORKSPACE
+    # lse, when given, must not overlap the output
+    st = lib.osx_attn_fwd_normalised(a, b, c, o, ctypes.c_void_p(0x400000 + 64), F32, 1, 1, 1, 16, 16, 64, 0, 0.0,
+                                     None, 0, None)
+    assert st == osx.OSX_EINVAL and "overlap" in osx.last_error()
+    assert lib.osx_attn_fwd_normalised(None, None, None, None, None, F32, 0, 4, 1, 16, 16, 64, 1, 0.0, None, 0,
+                                       None) == 0
+
+
 def test_softmax_rows_ex_rejects_before_launch():
     lib = osx.lib
     x, y = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x900000)

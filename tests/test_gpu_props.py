@@ -3,7 +3,8 @@
 Small shapes drawn over the whole argument space of each entry point --
 dtypes, GQA group sizes, causal or not, ragged sequence lengths, both head
 dims for bf16, column counts that take each softmax kernel (wavefront,
-workgroup, split), causal periods and scales -- against the fp64 oracle at the
+workgroup, split), causal periods and scales, the fp32 normalised-output
+variant with and without key splits -- against the fp64 oracle at the
 same bars as the fixed cases.  Outputs start NaN-poisoned, so every element
 must be written.
 """
@@ -118,3 +119,20 @@ def test_unfused_sweep(osx, hkv, groups, sq, sk, d, causal, seed):
     osx.attn_fwd_unfused(q, k, v, causal=causal, out=out)
     torch.cuda.synchronize()
     check(to_f64(out), oracle.attention(t["q"], t["k"], t["v"], causal=causal), "bf16", str(case))
+
+
+@settings(max_examples=15, deadline=None, derandomize=True, print_blob=True)
+@given(batch=st.integers(1, 2), hkv=st.integers(1, 2), groups=st.sampled_from([1, 2, 4]), sq=st.integers(1, 300),
+       sk=st.integers(1, 700), d=st.integers(1, 32), causal=st.booleans(), seed=st.integers(0, 2 ** 31 - 1))
+def test_normalised_sweep(osx, batch, hkv, groups, sq, sk, d, causal, seed):
+    if causal and sq > 1:
+        sk = sq
+    d *= 4
+    case = (batch, hkv, groups, sq, sk, d, causal, seed)
+    print(f"case sweep normalised {case}", flush=True)
+    t = synth.random_attn(seed, "f32", batch, hkv * groups, hkv, sq, sk, d)
+    q, k, v = to_dev(t["q"]), to_dev(t["k"]), to_dev(t["v"])
+    out = torch.full_like(q, float("nan"))
+    osx.attn_fwd_normalised(q, k, v, causal=causal, out=out)
+    torch.cuda.synchronize()
+    check(to_f64(out), oracle.attention(t["q"], t["k"], t["v"], causal=causal), "f32", str(case))
