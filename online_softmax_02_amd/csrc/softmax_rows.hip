@@ -280,38 +280,39 @@ __device__ __forceinline__ void normalise_chunk(const T* xb, T* yb, float m, flo
 // thread folds its visible values into (m, l); the states merge across the R
 // threads; the outputs come from the registers, so x is read once.  x and y
 // may be the same buffer: a row's reads all feed the merge, which comes before
-// its first store of a visible column, and its early stores (the masked
-// vectors) never overlap the vectors it reads.
+// its first store, and its zero stores (the masked vectors) never overlap the
+// vectors it reads.
 
 constexpr int kNonTemporal = 2;               // buffer-op cache policy: x and y are streamed once
 constexpr uint32_t kOffNowhere = 0x80000000u;  // a buffer offset past any row: the store is dropped
 
 // 16-byte path, first half of a row: load the nvis vectors that hold a visible
-// column (the buffer returns 0 past them) and store 0 to the masked vectors
-// (nvis <= vi < nv), which do not depend on x, while the loads are in flight.
-// The accesses are unconditional buffer operations, so the loads issue back to
-// back and the compiler's wait counts are exact.
+// column; the buffer returns 0 past them.  The loads are unconditional buffer
+// operations, so they issue back to back and the compiler's wait counts are
+// exact.
 template <typename T, int NV, int R>
-__device__ __forceinline__ void vec_issue(const T* xr, T* yr, uint32_t nvis, uint32_t nv, int t, u32x4 (&w)[NV]) {
+__device__ __forceinline__ void vec_issue(const T* xr, uint32_t nvis, int t, u32x4 (&w)[NV]) {
   const __amdgpu_buffer_rsrc_t xs = make_rsrc(xr, nvis * 16u);
 #pragma unroll
   for (int i = 0; i < NV; ++i)
     w[i] = __builtin_amdgcn_raw_buffer_load_b128(xs, 16u * (uint32_t)(t + R * i), 0, kNonTemporal);
-  const __amdgpu_buffer_rsrc_t zs = make_rsrc(yr, nv * 16u);
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const uint32_t vi = (uint32_t)(t + R * i);
-    __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, zs, vi >= nvis ? 16u * vi : kOffNowhere, 0,
-                                           kNonTemporal);
-  }
 }
 
 // Second half: (m, l) of the visible values (column < lim), merged over the
 // R threads; then y = 2^((x - m) k) / l for the nvis loaded vectors (0 for
-// their masked columns).
+// their masked columns).  Each thread keeps p = 2^((x - m_t) k) against its
+// own max m_t from the sum and scales it by 2^((m_t - m) k) / l for the
+// output, so every element takes one exponential.  Vector slot i holds
+// vectors t + R i of the R threads: when R i >= nvis no thread's slot-i vector
+// holds a visible column, and the slot's exponentials and stores are skipped
+// (a branch that is uniform over the group).  Last, 0 goes to the masked
+// vectors (nvis <= vi < nv), again through unconditional buffer stores: the
+// range check drops the visible ones.  (Issued after the row's own stores
+// rather than while its loads are in flight, they measured 3% faster on
+// causal bf16 rows of 2048 columns.)
 template <typename T, int NV, int R>
-__device__ __forceinline__ void vec_finish(T* yr, int lim, uint32_t nvis, int t, const u32x4 (&w)[NV], float k,
-                                           float* sm) {
+__device__ __forceinline__ void vec_finish(T* yr, int lim, uint32_t nvis, uint32_t nv, int t, const u32x4 (&w)[NV],
+                                           float k, float* sm) {
   using L = Elem<T>;
   constexpr int E = L::E, N = NV * E;
   float v[N];
@@ -326,21 +327,35 @@ __device__ __forceinline__ void vec_finish(T* yr, int lim, uint32_t nvis, int t,
   float m = v[0];
 #pragma unroll
   for (int j = 1; j < N; ++j) m = fmaxf(m, v[j]);
+  const float m_use = m == kNegInf ? 0.f : m;  // a thread with nothing visible: every p is 2^-inf = 0
   float l = 0.f;
-  if (m != kNegInf) {
 #pragma unroll
-    for (int j = 0; j < N; ++j) l += exp2_fast((v[j] - m) * k);  // -inf -> 0
+  for (int i = 0; i < NV; ++i) {
+    if ((uint32_t)(R * i) >= nvis) break;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      v[i * E + e] = exp2_fast((v[i * E + e] - m_use) * k);
+      l += v[i * E + e];
+    }
   }
   State s = {m, l};
   s = R == kWaveSize ? wave_merge(s, k) : block_merge(s, sm, k);
-  const float inv_l = 1.0f / s.l;
+  const float scale = m == kNegInf ? 0.f : exp2_fast((m - s.m) * k) / s.l;
   const __amdgpu_buffer_rsrc_t ys = make_rsrc(yr, nvis * 16u);
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
+    if ((uint32_t)(R * i) >= nvis) break;
     float f[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) f[e] = exp2_fast((v[i * E + e] - s.m) * k) * inv_l;
+    for (int e = 0; e < E; ++e) f[e] = v[i * E + e] * scale;
     __builtin_amdgcn_raw_buffer_store_b128(L::pack(f), ys, 16u * (uint32_t)(t + R * i), 0, kNonTemporal);
+  }
+  const __amdgpu_buffer_rsrc_t zs = make_rsrc(yr, nv * 16u);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const uint32_t vi = (uint32_t)(t + R * i);
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, zs, vi >= nvis ? 16u * vi : kOffNowhere, 0,
+                                           kNonTemporal);
   }
 }
 
@@ -387,8 +402,8 @@ __global__ __launch_bounds__(kThreads) void softmax_wave_kernel(const T* x, T* y
   if (VEC) {
     const uint32_t nvis = __builtin_amdgcn_readfirstlane((uint32_t)((lim + E - 1) / E));
     u32x4 w[NV];
-    vec_issue<T, NV, kWaveSize>(x + row * cols, y + row * cols, nvis, (uint32_t)(cols / E), t, w);
-    vec_finish<T, NV, kWaveSize>(y + row * cols, lim, nvis, t, w, k, nullptr);
+    vec_issue<T, NV, kWaveSize>(x + row * cols, nvis, t, w);
+    vec_finish<T, NV, kWaveSize>(y + row * cols, lim, nvis, (uint32_t)(cols / E), t, w, k, nullptr);
   } else {
     scalar_row<T, NV, kWaveSize>(x + row * cols, y + row * cols, lim, cols, t, k, nullptr);
   }
@@ -406,8 +421,8 @@ __global__ __launch_bounds__(kThreads) void softmax_row_kernel(const T* x, T* y,
   if (VEC) {
     const uint32_t nvis = __builtin_amdgcn_readfirstlane((uint32_t)((lim + E - 1) / E));
     u32x4 w[NV];
-    vec_issue<T, NV, kThreads>(x + row * cols, y + row * cols, nvis, (uint32_t)(cols / E), t, w);
-    vec_finish<T, NV, kThreads>(y + row * cols, (int)lim, nvis, t, w, k, sm);
+    vec_issue<T, NV, kThreads>(x + row * cols, nvis, t, w);
+    vec_finish<T, NV, kThreads>(y + row * cols, (int)lim, nvis, (uint32_t)(cols / E), t, w, k, sm);
   } else {
     scalar_row<T, NV, kThreads>(x + row * cols, y + row * cols, lim, cols, t, k, sm);
   }
