@@ -9,8 +9,9 @@ same run and reported under ``also``: GQA decode (GB/s over K/V), the long-row
 softmax and the causal bf16 score-row softmax (GB/s: the visible inputs read
 twice, or once where the row stays in registers, + 1 write), the two
 three-pass softmax comparators on the long row (with their time relative to
-the two-pass kernel), the fp32 4096^2 attention (TFLOP/s) and the two small
-latency cases (microseconds), and the unfused three-kernel attention
+the two-pass kernel), the fp32 4096^2 attention (TFLOP/s) with the plain and
+the normalised-output recurrence, the prefill with the log-sum-exp output, the
+two small latency cases (microseconds), and the unfused three-kernel attention
 comparator on the prefill workload (its time relative to the fused call).
 
 Inputs are seeded synthetic tensors (``synth``), generated on the host and
@@ -225,7 +226,7 @@ def bench_softmax_3pass(torch, osx, args, two_pass_us):
 
 
 def bench_softmax_causal(torch, osx, args):
-    """Causal bf16 score rows: one workgroup per row reads the visible columns and zero-fills the rest."""
+    """Causal bf16 score rows: one wavefront per row reads the visible columns and zero-fills the rest."""
     import synth
     w = synth.WORKLOADS["softmax_causal_bf16"]
     x = to_dev(synth.softmax_inputs(w))
