@@ -88,8 +88,13 @@ __global__ __launch_bounds__(kAttnThreads, 2) void decode_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, grp = lane >> 4;
 
-  const int split = blockIdx.x % splits;
-  const int bkv = blockIdx.x / splits;
+  // Workgroups are dealt to the 8 XCDs round-robin in launch order; numbering
+  // them so that each XCD streams a contiguous run of (b, KV head, split)
+  // units measured 1% faster than the launch order.
+  const int nwg = gridDim.x;
+  const int wg = nwg % 8 == 0 ? (int)((blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8) : (int)blockIdx.x;
+  const int split = wg % splits;
+  const int bkv = wg / splits;
   const int b = bkv / Hkv, kvh = bkv % Hkv;
   const int G = Hq / Hkv;
 
@@ -238,7 +243,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void decode_bf16_kernel(
   float* ws_ml = ws;
   const size_t n_part = (size_t)gridDim.x * G;
   float* ws_acc = ws + 2 * n_part;
-  const size_t part0 = (size_t)blockIdx.x * G;
+  const size_t part0 = (size_t)wg * G;
   for (int idx = tid; idx < G * D; idx += kAttnThreads) {
     const int col = idx / D, dd = idx % D;
     float M = kNegInf;
