@@ -35,6 +35,7 @@ namespace osx {
 namespace {
 
 constexpr int BN = kF32BlockN;  // 32 keys per block
+constexpr uint32_t kOffNowhere = 0x80000000u;  // a buffer offset past any head (heads are < 2^31 bytes)
 
 template <int DP>
 struct F32Tile {
@@ -85,7 +86,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_f32_kernel(
 
   const size_t q_base = (size_t)(b * Hq + head) * Sq * d;
   const size_t kv_base = (size_t)(b * Hkv + kvh) * Sk * d;
-  // Rows past Sq / Sk read as zeros; padded columns (d <= col < DP) are zeroed by a select.
+  // Rows past Sq / Sk read as zeros; so do the padded columns (d <= col < DP),
+  // whose loads are sent to an offset past the buffer.  (A select on the
+  // loaded value instead would make each load wait for its data where it is
+  // issued, exposing the next block's load latency in every block.)
   const __amdgpu_buffer_rsrc_t qr = make_rsrc(Qg + q_base, (uint32_t)Sq * d * 4);
   const __amdgpu_buffer_rsrc_t kr = make_rsrc(Kg + kv_base, (uint32_t)Sk * d * 4);
   const __amdgpu_buffer_rsrc_t vr = make_rsrc(Vg + kv_base, (uint32_t)Sk * d * 4);
@@ -95,8 +99,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_f32_kernel(
 #pragma unroll
   for (int j = 0; j < T::HALF; j += 4) {
     const int col = hf * T::HALF + j;
-    f32x4 x = buf_ld16f(qr, (uint32_t)(q * d + col) * 4);
-    if (col >= d) x = f32x4{};
+    const f32x4 x = buf_ld16f(qr, col < d ? (uint32_t)(q * d + col) * 4 : kOffNowhere);
     qv[j] = x.x;
     qv[j + 1] = x.y;
     qv[j + 2] = x.z;
@@ -121,13 +124,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_f32_kernel(
     for (int r = 0; r < T::PER_T; ++r) {
       const int u = tid + kAttnThreads * r;
       const int key = u / T::CH, col = (u % T::CH) * 4;
-      const uint32_t off = (uint32_t)((j0 + key) * d + col) * 4;
+      const uint32_t off = col < d ? (uint32_t)((j0 + key) * d + col) * 4 : kOffNowhere;
       kst[r] = buf_ld16f(kr, off);
       vst[r] = buf_ld16f(vr, off);
-      if (col >= d) {
-        kst[r] = f32x4{};
-        vst[r] = f32x4{};
-      }
     }
   };
   auto store_block = [&](int buf) {
