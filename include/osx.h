@@ -87,7 +87,12 @@ typedef struct osx_plan {
 int osx_attn_plan(int dtype, int batch, int heads_q, int heads_kv, int seq_q, int seq_k, int head_dim, int causal,
                   osx_plan* out);
 
-/* Workspace bytes osx_attn_fwd needs for this problem (0 for prefill), via *bytes. */
+/*
+ * Workspace bytes osx_attn_fwd needs for this problem, via *bytes: the partial
+ * (m, l, acc) states when the keys are split across workgroups (fp32 with few
+ * row tiles, decode with few (batch, KV head) units); 0 otherwise (bf16
+ * prefill, and decode that runs as one split).
+ */
 int osx_attn_fwd_workspace(int dtype, int batch, int heads_q, int heads_kv, int seq_q, int seq_k, int head_dim,
                            int causal, size_t* bytes);
 

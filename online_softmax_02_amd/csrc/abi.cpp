@@ -75,7 +75,8 @@ int plan_attn(int dtype, int batch, int heads_q, int heads_kv, int seq_q, int se
     p->splits = (int)splits;
     p->heads_per_wg = groups;
     p->grid = units * splits;
-    p->workspace_bytes = (size_t)(units * splits * groups) * (size_t)(2 + head_dim) * sizeof(float);
+    // One split writes O directly; more write partial states for the combine kernel.
+    p->workspace_bytes = splits == 1 ? 0 : (size_t)(units * splits * groups) * (size_t)(2 + head_dim) * sizeof(float);
     return ok();
   }
   const int hp = heads_per_wg(groups);

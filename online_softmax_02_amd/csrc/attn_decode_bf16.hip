@@ -12,11 +12,12 @@
 //    two workgroups per CU.  K feeds S^T = K Q^T directly from registers; V is written
 //    to the wavefront's LDS slice transposed (keys permuted so each lane's 8
 //    keys are one 16-byte read) and feeds O^T += V^T P^T.
-//  * The 4 wavefront states are merged in LDS and written as one partial
-//    (m, l, acc) per split.  A second kernel merges the splits of each query
-//    head with the rule of page "Softmax 算子的实现与优化", section Online
-//    Softmax, applied to partial states: m = max m_s, l = sum l_s 2^(m_s - m),
-//    acc = sum acc_s 2^(m_s - m), then O = acc / l.
+//  * The 4 wavefront states are merged in LDS.  With one split that state is
+//    final and the workgroup writes O = acc / l itself; otherwise it writes
+//    one partial (m, l, acc) per split and a second kernel merges the splits
+//    of each query head with the rule of page "Softmax 算子的实现与优化",
+//    section Online Softmax, applied to partial states: m = max m_s,
+//    l = sum l_s 2^(m_s - m), acc = sum acc_s 2^(m_s - m), then O = acc / l.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -76,7 +77,8 @@ __device__ __forceinline__ void load_regs(Regs<D>& R, __amdgpu_buffer_rsrc_t kr,
 template <int D>
 __global__ __launch_bounds__(kAttnThreads, 2) void decode_bf16_kernel(
     const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, const uint16_t* __restrict__ Vg,
-    float* __restrict__ ws, int Hq, int Hkv, int Sk, float c, int splits, int keys_per_split) {
+    float* __restrict__ ws, uint16_t* __restrict__ Og, float* __restrict__ Lse, int Hq, int Hkv, int Sk, float c,
+    int splits, int keys_per_split) {
   using T = DecTile<D>;
   // V^T slices during the stream; reused for the wavefront merge afterwards.
   constexpr int MERGE_BYTES = kAttnWaves * NCOL * (D + 2) * 4;
@@ -258,10 +260,19 @@ __global__ __launch_bounds__(kAttnThreads, 2) void decode_bf16_kernel(
         asum += accl[(w * NCOL + col) * D + dd] * f;
       }
     }
-    ws_acc[(part0 + col) * D + dd] = asum;
-    if (dd == 0) {
-      ws_ml[(part0 + col) * 2] = M;
-      ws_ml[(part0 + col) * 2 + 1] = lsum;
+    if (splits == 1) {
+      // The workgroup saw every key: its merged state is final, O = acc / l.
+      // (Every key split holds at least one key, so l > 0.)
+      const size_t bh = (size_t)b * Hq + kvh * G + col;
+      Og[bh * D + dd] = (uint16_t)(pack_bf16x2(asum / lsum, 0.f) & 0xffffu);
+      // log sum_j exp(scale * s_j) = ln 2 * (M + log2 l), M in the log2 domain
+      if (Lse && dd == 0) Lse[bh] = (M + log2f(lsum)) * kLn2;
+    } else {
+      ws_acc[(part0 + col) * D + dd] = asum;
+      if (dd == 0) {
+        ws_ml[(part0 + col) * 2] = M;
+        ws_ml[(part0 + col) * 2 + 1] = lsum;
+      }
     }
   }
 }
@@ -325,9 +336,10 @@ hipError_t launch(const AttnArgs& a) {
   float* ws = static_cast<float*>(a.workspace);
   hipLaunchKernelGGL(decode_bf16_kernel<D>, dim3((unsigned)a.plan.grid), dim3(kAttnThreads), 0, a.stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                     static_cast<const uint16_t*>(a.v), ws, a.heads_q, a.heads_kv, a.seq_k, a.c, splits, kps);
+                     static_cast<const uint16_t*>(a.v), ws, static_cast<uint16_t*>(a.o), a.lse, a.heads_q, a.heads_kv,
+                     a.seq_k, a.c, splits, kps);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || splits == 1) return e;
   hipLaunchKernelGGL(decode_combine_kernel<D>, dim3((unsigned)(a.batch * a.heads_q)), dim3(D), 0, a.stream, ws,
                      static_cast<uint16_t*>(a.o), a.lse, a.heads_q, a.heads_kv, splits, (int)a.plan.grid);
   return hipGetLastError();

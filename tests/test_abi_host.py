@@ -58,11 +58,15 @@ def test_attn_fwd_rejects_before_launch():
     # null pointers with work to do
     st = lib.osx_attn_fwd(None, None, None, None, BF16, 1, 4, 1, 16, 16, 128, 0, 0.0, None, 0, None)
     assert st == osx.OSX_EINVAL and "null" in osx.last_error()
-    # decode needs a workspace
+    # decode with its keys split needs a workspace for the partial states
     fake = ctypes.c_void_p(0x1000)
+    assert osx.attn_plan(BF16, 1, 4, 1, 1, 8192, 128)["splits"] > 1
     st = lib.osx_attn_fwd(fake, ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000), ctypes.c_void_p(0x300000),
-                          BF16, 2, 8, 2, 1, 64, 128, 0, 0.0, None, 0, None)
+                          BF16, 1, 4, 1, 1, 8192, 128, 0, 0.0, None, 0, None)
     assert st == osx.OSX_EWORKSPACE
+    # one split writes O directly and needs none
+    p = osx.attn_plan(BF16, 2, 8, 2, 1, 64, 128)
+    assert p["splits"] == 1 and p["workspace_bytes"] == 0
     # output aliasing an input
     st = lib.osx_attn_fwd(fake, ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000), fake,
                           F32, 1, 1, 1, 16, 16, 64, 0, 0.0, None, 0, None)
@@ -96,7 +100,8 @@ def test_plans_for_the_workloads():
     p = osx.attn_plan(BF16, 64, 32, 8, 1, 8192, 128)
     assert p["kernel_name"] == "decode_bf16"
     assert p["workspace_bytes"] == osx.attn_fwd_workspace(BF16, 64, 32, 8, 1, 8192, 128)
-    assert p["workspace_bytes"] == 64 * 8 * p["splits"] * 4 * (2 + 128) * 4
+    want = 0 if p["splits"] == 1 else 64 * 8 * p["splits"] * 4 * (2 + 128) * 4
+    assert p["workspace_bytes"] == want
     p = osx.attn_plan(F32, 1, 1, 1, 64, 100, 48)
     assert p["kernel_name"] == "prefill_f32" and p["grid"] == 1 and p["splits"] == 1
     p = osx.attn_plan(F32, 1, 1, 1, 4096, 4096, 128)  # one head: the keys are split to fill the GPU
