@@ -39,20 +39,30 @@ constexpr uint32_t kOffNowhere = 0x80000000u;  // a buffer offset past any head 
 
 template <int DP>
 struct F32Tile {
-  static constexpr int CH = DP / 4;                 // 16-byte chunks per K row
+  static constexpr int CH = DP / 4;                 // 16-byte chunks per K or V row
   static constexpr int HALF = DP / 2;               // d values per MFMA half-wave
   static constexpr int DT = DP / 32;                // 32-row d tiles of the PV MFMA
-  static constexpr int VSTRIDE = DP + 8;            // padded V row (floats)
-  static constexpr int K_BYTES = BN * DP * 4;
-  static constexpr int V_BYTES = BN * VSTRIDE * 4;
-  static constexpr int BUF = K_BYTES + V_BYTES;
-  static constexpr int UNITS = BN * CH;             // 16-byte units per block (K or V)
-  static constexpr int PER_T = (UNITS + kAttnThreads - 1) / kAttnThreads;
+  static constexpr int ROW = DP * 4;                // bytes per K or V row in LDS
+  static constexpr int BLOCK_BYTES = BN * ROW;      // one K or V block
+  static constexpr int DMA_PER_WAVE = BLOCK_BYTES / 1024 / kAttnWaves;  // 1-KiB loads per wavefront per block
 };
+static_assert(F32Tile<32>::DMA_PER_WAVE * 1024 * kAttnWaves == F32Tile<32>::BLOCK_BYTES, "whole 1-KiB loads");
+static_assert(F32Tile<96>::DMA_PER_WAVE * 1024 * kAttnWaves == F32Tile<96>::BLOCK_BYTES, "whole 1-KiB loads");
 
+// Chunk swizzles (16-byte chunk index XOR a function of the row).  K: the QK
+// read takes one chunk of each of 32 consecutive rows.  V: the PV read takes 8
+// consecutive chunks of row key (lanes 0-31) and of row key + 4 (lanes 32-63);
+// flipping bit 3 of the chunk index on rows with bit 2 set puts the two halves
+// in opposite halves of the banks (when a row holds a multiple of 16 chunks;
+// otherwise V is not swizzled and that read is 2-way conflicted).  Both XORs
+// stay inside the row.
 template <int CH>
 __device__ __forceinline__ int k_swz(int row) {
   return CH % 16 == 0 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int CH>
+__device__ __forceinline__ int v_swz(int row) {
+  return CH % 16 == 0 ? ((row >> 2) & 1) << 3 : 0;
 }
 
 template <int DP, bool NORM>
@@ -62,7 +72,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_f32_kernel(
     int n_qtiles, int units_per_tile, int splits, int keys_per_split, float* __restrict__ ws_ml,
     float* __restrict__ ws_acc) {
   using T = F32Tile<DP>;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * T::BUF];
+  // Two K blocks, then two V blocks.
+  __shared__ __attribute__((aligned(16))) unsigned char lds[4 * T::BLOCK_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -115,33 +126,39 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_f32_kernel(
   if (n_keys > k_begin + keys_per_split) n_keys = k_begin + keys_per_split;
   const int jb0 = k_begin / BN;
   const int nblk = (n_keys + BN - 1) / BN;
-  const int wave_row_last = row0 + kRowsPerWave - 1;
   const size_t row_id = (size_t)(b * Hq + head) * Sq + q;  // partial-state row (split mode)
 
-  f32x4 kst[T::PER_T], vst[T::PER_T];
-  auto load_block = [&](int j0) {
+  // K and V pass through separate double-buffered LDS blocks, K one block
+  // further ahead than V: while block j's weights are formed and multiplied
+  // by V(j), the scores of block j + 1 are already computed (from K(j + 1)),
+  // so the softmax arithmetic of one block runs under the matrix products of
+  // the next.  Blocks are copied with direct-to-LDS buffer loads: a 16-byte
+  // load of lane i lands at M0 + 16 i, so each lane fetches the global chunk
+  // that belongs in its swizzled slot; padded columns (d <= col < DP) and rows
+  // past Sk read as zeros.
+  unsigned char* const lds_k = lds;
+  unsigned char* const lds_v = lds + 2 * T::BLOCK_BYTES;
+  // Lane offset of load n of this wavefront within a block (row-major rows of
+  // d floats in global memory), or an offset past the buffer for a padded column.
+  auto dma_voff = [&](int n, bool is_v) -> uint32_t {
+    const int pos = (n * kAttnWaves + wave) * 1024 + 16 * lane;  // byte in the block
+    const int row = pos / T::ROW, slot = (pos % T::ROW) >> 4;
+    const int ch = slot ^ (is_v ? v_swz<T::CH>(row) : k_swz<T::CH>(row));
+    return 4 * ch < d ? (uint32_t)(row * d + 4 * ch) * 4 : kOffNowhere;
+  };
+  auto dma = [&](__amdgpu_buffer_rsrc_t rsrc, bool is_v, unsigned char* dst, int j0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int r = 0; r < T::PER_T; ++r) {
-      const int u = tid + kAttnThreads * r;
-      const int key = u / T::CH, col = (u % T::CH) * 4;
-      const uint32_t off = col < d ? (uint32_t)((j0 + key) * d + col) * 4 : kOffNowhere;
-      kst[r] = buf_ld16f(kr, off);
-      vst[r] = buf_ld16f(vr, off);
+    for (int n = 0; n < T::DMA_PER_WAVE; ++n) {
+      const int inst = n * kAttnWaves + wave;  // uniform
+      const uint32_t voff = dma_voff(n, is_v);
+      // block offset, uniform (an offset past the range stays past it)
+      const int soff = j0 * d * 4;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(dst + inst * 1024),
+                                               16, voff, soff, 0, 0);
     }
   };
-  auto store_block = [&](int buf) {
-    unsigned char* kl = lds + buf * T::BUF;
-    float* vl = reinterpret_cast<float*>(kl + T::K_BYTES);
-#pragma unroll
-    for (int r = 0; r < T::PER_T; ++r) {
-      const int u = tid + kAttnThreads * r;
-      if (u < T::UNITS) {
-        const int key = u / T::CH, ch = u % T::CH;
-        *reinterpret_cast<f32x4*>(kl + key * (DP * 4) + ((ch ^ k_swz<T::CH>(key)) << 4)) = kst[r];
-        *reinterpret_cast<f32x4*>(vl + key * T::VSTRIDE + ch * 4) = vst[r];
-      }
-    }
-  };
+  auto load_k = [&](int j0, int buf) { dma(kr, false, lds_k + buf * T::BLOCK_BYTES, j0); };
+  auto load_v = [&](int j0, int buf) { dma(vr, true, lds_v + buf * T::BLOCK_BYTES, j0); };
 
   f32x16 acc[T::DT];
 #pragma unroll
@@ -161,94 +178,126 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_f32_kernel(
     return;
   }
 
-  // Every slice that is not empty starts with a visible key for every row.
-  load_block(jb0 * BN);
-  store_block(jb0 & 1);
+  // S^T = K Q^T over the padded head dimension, from K block buffer `buf`.
+  auto qk = [&](int buf) {
+    const unsigned char* kl = lds_k + buf * T::BLOCK_BYTES;
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int j = 0; j < T::HALF; j += 4) {
+      const int ch = (hf * T::HALF + j) >> 2;
+      const f32x4 a = *reinterpret_cast<const f32x4*>(kl + l32 * (DP * 4) + ((ch ^ k_swz<T::CH>(l32)) << 4));
+      s = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, qv[j], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, qv[j + 1], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, qv[j + 2], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, qv[j + 3], s, 0, 0, 0);
+    }
+    return s;
+  };
+
+  // The last key this lane's row may see: keys past Sk and (causal) after the
+  // row are masked to -inf.  The mask is applied to every block without a
+  // branch, so that a block's softmax and the next block's QK products form
+  // one straight-line region the compiler can interleave.  A block wholly
+  // after a wavefront's rows (causal) then gives p = 0 everywhere and leaves
+  // the state unchanged.
+  const int key_last = cmask ? (q < Sk - 1 ? q : Sk - 1) : Sk - 1;
+
+  // Softmax of block j0's scores s (in place: s becomes the weights P) and the
+  // update of m and l; returns the factor the accumulator must be multiplied
+  // by (applied by rescale(), outside the straight-line region).
+  auto softmax = [&](f32x16& s, int j0) -> float {
+    const int rel = key_last - j0 - 4 * hf;  // key j0 + 8 (r / 4) + 4 hf + r % 4 is visible iff 8 (r / 4) + r % 4 <= rel
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 8 * (r >> 2) + (r & 3) <= rel ? s[r] : kNegInf;
+    float mx = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mx = pair_max(mx);
+    const float m_new = fmaxf(m_run, mx * c);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = exp2_fast(m_run - m_use);
+    float rsum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = exp2_fast(fmaf(s[r], c, -m_use));
+      s[r] = p;
+      rsum += p;
+    }
+    if constexpr (NORM) {
+      // d'_new = d'_old 2^(m_old - m_new) + the block's sum over both halves
+      // of the row (l_run holds the whole row's d' in both halves).  A row
+      // with nothing visible yet keeps d' = 0 and an all-zero accumulator.
+      const float d_new = l_run * alpha + pair_sum(rsum);
+      const float inv_d = d_new > 0.f ? 1.0f / d_new : 0.f;
+      const float beta = l_run * alpha * inv_d;  // (d'_old / d'_new) 2^(m_old - m_new)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] *= inv_d;
+      l_run = d_new;
+      m_run = m_new;
+      return beta;
+    } else {
+      l_run = l_run * alpha + rsum;
+      m_run = m_new;
+      return alpha;
+    }
+  };
+  // acc *= f; without NORM only when some row's max moved (f != 1), which is
+  // rare once the first blocks are seen.
+  auto rescale = [&](float f) {
+    if (NORM || __ballot(f != 1.0f)) {
+#pragma unroll
+      for (int i = 0; i < T::DT; ++i) acc[i] *= f;
+    }
+  };
+
+  // O^T += V^T P^T from V block buffer `buf`: lane (d, hf) reads V[key(r, hf)][d],
+  // stored in chunk (d / 4) ^ v_swz(key) of its row.
+  auto pv = [&](const f32x16& s, int buf) {
+    const float* vl = reinterpret_cast<const float*>(lds_v + buf * T::BLOCK_BYTES);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 8 * (r >> 2) + 4 * hf + (r & 3);
+#pragma unroll
+      for (int dt = 0; dt < T::DT; ++dt) {
+        const int col = 32 * dt + l32;
+        const float a = vl[key * DP + ((((col >> 2) ^ v_swz<T::CH>(key)) << 2) | (col & 3))];
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[r], acc[dt], 0, 0, 0);
+      }
+    }
+  };
+
+  // Prologue: K and V of the first block, K of the second.  Every slice that
+  // is not empty starts with a visible key for every row.
+  load_k(jb0 * BN, jb0 & 1);
+  load_v(jb0 * BN, jb0 & 1);
+  if (jb0 + 1 < nblk) load_k((jb0 + 1) * BN, (jb0 + 1) & 1);
   wait_vmem();
+  __syncthreads();
+  f32x16 s_cur = qk(jb0 & 1);
+  // The first iteration reloads this K buffer (with block jb0 + 2): every
+  // wavefront must have read it first.
   __syncthreads();
 
   for (int jb = jb0; jb < nblk; ++jb) {
     const int j0 = jb * BN;
-    const bool has_next = jb + 1 < nblk;
-    if (has_next) load_block(j0 + BN);
-
-    const bool active = !(cmask && j0 > wave_row_last);
-    if (active) {
-      const unsigned char* kl = lds + (jb & 1) * T::BUF;
-      const float* vl = reinterpret_cast<const float*>(kl + T::K_BYTES);
-
-      // S^T = K Q^T over the padded head dimension
-      f32x16 s = f32x16{};
-#pragma unroll
-      for (int j = 0; j < T::HALF; j += 4) {
-        const int ch = (hf * T::HALF + j) >> 2;
-        const f32x4 a = *reinterpret_cast<const f32x4*>(kl + l32 * (DP * 4) + ((ch ^ k_swz<T::CH>(l32)) << 4));
-        s = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, qv[j], s, 0, 0, 0);
-        s = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, qv[j + 1], s, 0, 0, 0);
-        s = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, qv[j + 2], s, 0, 0, 0);
-        s = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, qv[j + 3], s, 0, 0, 0);
-      }
-
-      const bool need_mask = (j0 + BN > Sk) || (cmask && j0 + BN - 1 > row0);
-      if (need_mask) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kidx = j0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          const bool ok = kidx < Sk && (!cmask || kidx <= q);
-          s[r] = ok ? s[r] : kNegInf;
-        }
-      }
-
-      float mx = s[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx * c);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = exp2_fast(m_run - m_use);
-      float rsum = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2_fast(fmaf(s[r], c, -m_use));
-        s[r] = p;
-        rsum += p;
-      }
-      if constexpr (NORM) {
-        // d'_new = d'_old 2^(m_old - m_new) + the block's sum over both halves
-        // of the row (l_run holds the whole row's d' in both halves).  A row
-        // with nothing visible yet keeps d' = 0 and an all-zero accumulator.
-        const float d_new = l_run * alpha + (rsum + __shfl_xor(rsum, 32, 64));
-        const float inv_d = d_new > 0.f ? 1.0f / d_new : 0.f;
-        const float beta = l_run * alpha * inv_d;  // (d'_old / d'_new) 2^(m_old - m_new)
-#pragma unroll
-        for (int i = 0; i < T::DT; ++i) acc[i] *= beta;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] *= inv_d;
-        l_run = d_new;
-      } else {
-        l_run = l_run * alpha + rsum;
-        if (__ballot(alpha != 1.0f)) {
-#pragma unroll
-          for (int i = 0; i < T::DT; ++i) acc[i] *= alpha;
-        }
-      }
-      m_run = m_new;
-
-      // O^T += V^T P^T: lane (d, hf) reads V[key(r, hf)][d]
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 8 * (r >> 2) + 4 * hf + (r & 3);
-#pragma unroll
-        for (int dt = 0; dt < T::DT; ++dt) {
-          const float a = vl[key * T::VSTRIDE + 32 * dt + l32];
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[r], acc[dt], 0, 0, 0);
-        }
-      }
+    const bool has1 = jb + 1 < nblk, has2 = jb + 2 < nblk;
+    // K(jb + 2) replaces K(jb) and V(jb + 1) replaces V(jb - 1): both were
+    // last read before the previous barrier.
+    if (has2) load_k(j0 + 2 * BN, jb & 1);
+    if (has1) load_v(j0 + BN, (jb + 1) & 1);
+    f32x16 s_next = f32x16{};
+    float f;
+    if (has1) {
+      s_next = qk((jb + 1) & 1);
+      f = softmax(s_cur, j0);
+    } else {
+      f = softmax(s_cur, j0);
     }
-
-    if (has_next) store_block((jb + 1) & 1);
+    rescale(f);
+    pv(s_cur, jb & 1);
     wait_vmem();
     __syncthreads();
+    s_cur = s_next;
   }
 
   const float l_tot = NORM ? l_run : l_run + __shfl_xor(l_run, 32, 64);
