@@ -11,8 +11,10 @@ twice, or once where the row stays in registers, + 1 write), the two
 three-pass softmax comparators on the long row (with their time relative to
 the two-pass kernel), the fp32 4096^2 attention (TFLOP/s) with the plain and
 the normalised-output recurrence, the prefill with the log-sum-exp output, the
-two small latency cases (microseconds), and the unfused three-kernel attention
-comparator on the prefill workload (its time relative to the fused call).
+two small latency cases (microseconds), the unfused three-kernel attention
+comparator on the prefill workload (its time relative to the fused call), and,
+as the reference for the HBM-bound lines, a plain 16-byte streaming read of
+2 GiB on the same GPU.
 
 Inputs are seeded synthetic tensors (``synth``), generated on the host and
 copied to HBM before timing.  Durations come from one HIP event pair recorded
@@ -52,7 +54,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--only", default="all",
-                   choices=["all", "prefill", "unfused", "decode", "softmax", "f32", "small", "copy"],
+                   choices=["all", "prefill", "unfused", "decode", "softmax", "f32", "small", "copy", "probe"],
                    help="time one workload only (for profiler runs)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle timing sample")
@@ -297,6 +299,18 @@ def bench_small(torch, osx, args):
     return res
 
 
+def bench_read_probe(torch, osx, args):
+    """Context for the HBM-bound lines: a plain 16-byte streaming read of 2 GiB (osx_read_probe) on the same GPU."""
+    n = 1 << 29
+    x = torch.ones(n, dtype=torch.int32, device="cuda")
+    sink = torch.empty(osx.lib.osx_read_probe_sink_bytes() // 4, dtype=torch.int32, device="cuda")
+    _, ms = timed(torch, lambda i: osx.read_probe(x, sink=sink), args.steps, args.warmup)
+    gbs = 4.0 * n / (ms * 1e-3) / 1e9
+    return {"workload": "read 2 GiB", "unit": "GB/s", "value": round(gbs, 1), "call_us": round(ms * 1e3, 2),
+            "note": "achievable-bandwidth reference (loads only), not a step of the method",
+            "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", None)}
+
+
 def bench_copy(torch, args):
     """A plain device copy of known size (256 MiB), to calibrate the HBM byte counters."""
     n = 64 << 20
@@ -346,6 +360,9 @@ def main():
         print(json.dumps({"copy": bench_copy(torch, args)}))
         return
     also = {}
+    if args.only == "probe":
+        print(json.dumps({"also": {"hbm_read_probe": bench_read_probe(torch, osx, args)}}))
+        return
     if args.only in ("decode",):
         also["gqa_decode_bf16"] = bench_decode(torch, osx, args)
         print(json.dumps({"also": also}))
@@ -380,6 +397,8 @@ def main():
         print(json.dumps({"also": also}))
         return
     if args.only == "all":
+        also["hbm_read_probe"] = bench_read_probe(torch, osx, args)
+        log(f"[bench] plain streaming read {also['hbm_read_probe']['value']} GB/s")
         also["gqa_decode_bf16"] = bench_decode(torch, osx, args)
         log(f"[bench] decode {also['gqa_decode_bf16']['value']} GB/s")
         also["softmax_1x16m"] = bench_softmax(torch, osx, args)

@@ -53,7 +53,7 @@ extern "C" {
 #define OSX_KERNEL_NONE 0          /* no work */
 #define OSX_KERNEL_PREFILL_F32 1   /* fp32 MFMA tiles, any seq_q */
 #define OSX_KERNEL_PREFILL_BF16 2  /* bf16 MFMA tiles, any seq_q */
-#define OSX_KERNEL_DECODE_BF16 3   /* bf16, seq_q == 1: K/V split across workgroups + combine */
+#define OSX_KERNEL_DECODE_BF16 3   /* bf16, seq_q == 1: K/V split across workgroups (+ combine when split) */
 #define OSX_KERNEL_SOFTMAX_ROW 4   /* one workgroup per row, the row held in registers */
 #define OSX_KERNEL_SOFTMAX_SPLIT 5 /* rows split across workgroups, (m, l) partials merged */
 #define OSX_KERNEL_SOFTMAX_WAVE 6  /* one wavefront per row, the row held in registers */
@@ -243,6 +243,21 @@ int osx_softmax_rows_3pass_workspace(int64_t rows, int64_t cols, int method, siz
 
 int osx_softmax_rows_3pass(const float* x, float* y, int64_t rows, int64_t cols, int method, void* workspace,
                            size_t workspace_bytes, void* stream);
+
+/*
+ * osx_read_probe -- a measurement aid, not a step of the method: a plain
+ * streaming read of `bytes` of device memory at x (16-byte aligned, bytes a
+ * multiple of 16) with 16-byte non-temporal loads, each word read once.  The
+ * benchmark times it beside the HBM-bound kernels as the bandwidth that loads
+ * alone reach on the same GPU.  Every word read is folded into an XOR, one
+ * 32-bit word per wavefront written to `sink` (a device buffer of at least
+ * osx_read_probe_sink_bytes() bytes, not overlapping x): the XOR of all sink
+ * words equals the XOR of all words of x.  bytes == 0: OSX_OK, nothing
+ * launched.  Errors: null pointers or misalignment -> OSX_EINVAL, short sink
+ * -> OSX_EWORKSPACE.
+ */
+size_t osx_read_probe_sink_bytes(void);
+int osx_read_probe(const void* x, size_t bytes, void* sink, size_t sink_bytes, void* stream);
 
 /* Static text for a status code. */
 const char* osx_status_string(int status);

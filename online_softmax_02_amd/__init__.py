@@ -67,6 +67,10 @@ def _load() -> ctypes.CDLL:
     lib.osx_attn_fwd_unfused.argtypes = [_vp, _vp, _vp, _vp] + attn_shape + [_f, _vp, _sz, _vp]
     lib.osx_softmax_rows_3pass_workspace.argtypes = [_i64, _i64, _i, ctypes.POINTER(_sz)]
     lib.osx_softmax_rows_3pass.argtypes = [_vp, _vp, _i64, _i64, _i, _vp, _sz, _vp]
+    lib.osx_read_probe_sink_bytes.argtypes = []
+    lib.osx_read_probe_sink_bytes.restype = _sz
+    lib.osx_read_probe.argtypes = [_vp, _sz, _vp, _sz, _vp]
+    lib.osx_read_probe.restype = _i
     lib.osx_status_string.argtypes = [_i]
     lib.osx_status_string.restype = ctypes.c_char_p
     lib.osx_last_error.argtypes = []
@@ -334,7 +338,23 @@ def softmax_rows_3pass(x, method: int, out=None, workspace=None, stream=None):
     return out
 
 
+def read_probe(x, sink=None, stream=None):
+    """Plain streaming read of the contiguous CUDA tensor x (osx_read_probe: a measurement aid).
+
+    Returns the int32 sink tensor: the XOR of its words is the XOR of x's 32-bit words."""
+    torch = _torch()
+    if not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous CUDA tensor")
+    nbytes = x.numel() * x.element_size()
+    if sink is None:
+        sink = torch.empty(lib.osx_read_probe_sink_bytes() // 4, dtype=torch.int32, device=x.device)
+    _check(lib.osx_read_probe(x.data_ptr(), nbytes, sink.data_ptr(), sink.numel() * sink.element_size(),
+                              _stream(x, stream)))
+    return sink
+
+
 __all__ = ["attn_fwd", "softmax_rows", "attn_plan", "attn_fwd_workspace", "softmax_rows_plan",
            "softmax_rows_workspace", "status_string", "last_error", "version", "OsxError", "lib", "LIB_PATH",
            "OSX_F32", "OSX_BF16", "softmax_rows_3pass", "softmax_rows_3pass_workspace", "OSX_3PASS_ATOMIC",
-           "OSX_3PASS_STASH", "attn_fwd_unfused", "attn_fwd_unfused_workspace", "attn_fwd_normalised"]
+           "OSX_3PASS_STASH", "attn_fwd_unfused", "attn_fwd_unfused_workspace", "attn_fwd_normalised",
+           "read_probe"]

@@ -26,6 +26,7 @@ SOURCES = [
     "attn_prefill_f32.hip",
     "attn_decode_bf16.hip",
     "attn_unfused.hip",
+    "read_probe.hip",
 ]
 
 ARCH = "gfx950"

@@ -456,6 +456,21 @@ int osx_softmax_rows_3pass(const float* x, float* y, int64_t rows, int64_t cols,
   return ok();
 }
 
+size_t osx_read_probe_sink_bytes(void) { return osx::kProbeSinkBytes; }
+
+int osx_read_probe(const void* x, size_t bytes, void* sink, size_t sink_bytes, void* stream) {
+  if (bytes == 0) return ok();
+  if (!x || !sink) return fail(OSX_EINVAL, "null x or sink pointer");
+  if ((reinterpret_cast<uintptr_t>(x) & 15) || (bytes & 15))
+    return fail(OSX_EINVAL, "x must be 16-byte aligned and bytes a multiple of 16 (got %zu)", bytes);
+  if (sink_bytes < osx::kProbeSinkBytes)
+    return fail(OSX_EWORKSPACE, "sink of %zu bytes given, %zu needed", sink_bytes, osx::kProbeSinkBytes);
+  if (overlap(x, bytes, sink, osx::kProbeSinkBytes)) return fail(OSX_EINVAL, "sink overlaps x");
+  hipError_t e = osx::launch_read_probe(x, bytes, sink, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(OSX_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 const char* osx_status_string(int status) {
   switch (status) {
     case OSX_OK: return "OSX_OK";

@@ -73,6 +73,13 @@ struct Softmax3PassArgs {
   hipStream_t stream;
 };
 
+// Plain streaming read (a measurement reference): kProbeWgs workgroups of
+// kProbeThreads threads; the sink takes one 32-bit word per wavefront.
+constexpr int kProbeWgs = 2048;
+constexpr int kProbeThreads = 256;
+constexpr size_t kProbeSinkBytes = (size_t)kProbeWgs * (kProbeThreads / 64) * 4;
+hipError_t launch_read_probe(const void* x, size_t bytes, void* sink, hipStream_t stream);
+
 hipError_t launch_prefill_bf16(const AttnArgs& a);
 hipError_t launch_prefill_f32(const AttnArgs& a);
 hipError_t launch_decode_bf16(const AttnArgs& a);

@@ -206,3 +206,17 @@ def test_plan_rejects_heads_beyond_32_bit_addressing():
         osx.attn_plan(F32, 1, 1, 1, 1, 1 << 22, 128)  # decode-shaped, K of 2^31 bytes
     assert osx.attn_plan(BF16, 1, 1, 1, 1, (1 << 23) - 1, 128)["kernel_name"] == "decode_bf16"
     assert osx.attn_plan(F32, 1, 1, 1, 1000, (1 << 22) - 1, 128)["kernel_name"] == "prefill_f32"
+
+
+def test_read_probe_rejects_before_launch():
+    lib = osx.lib
+    need = lib.osx_read_probe_sink_bytes()
+    assert need == 2048 * 4 * 4
+    x, sink = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x900000)
+    assert lib.osx_read_probe(x, 0, None, 0, None) == 0  # nothing to read
+    assert lib.osx_read_probe(None, 1024, sink, need, None) == osx.OSX_EINVAL
+    assert lib.osx_read_probe(ctypes.c_void_p(0x100004), 1024, sink, need, None) == osx.OSX_EINVAL
+    assert lib.osx_read_probe(x, 1000, sink, need, None) == osx.OSX_EINVAL
+    assert lib.osx_read_probe(x, 1024, sink, need - 1, None) == osx.OSX_EWORKSPACE
+    assert lib.osx_read_probe(x, 1 << 20, ctypes.c_void_p(0x100000 + 4096), need, None) == osx.OSX_EINVAL
+    assert "overlap" in osx.last_error()
