@@ -9,7 +9,7 @@
 // loses precision).
 //
 // Each MFMA lane supplies a single k value, so P^T comes straight from the
-// score registers and V is read from a plain row-major LDS block.  The head
+// score registers and V is read from a row-major (chunk-swizzled) LDS block.  The head
 // dimension d (a multiple of 4, at most 128) is padded with zeros up to DP,
 // a multiple of 32; padded columns are never stored.  Blocks are 32 keys.
 //
