@@ -197,9 +197,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_f32_kernel(
   // The last key this lane's row may see: keys past Sk and (causal) after the
   // row are masked to -inf.  The mask is applied to every block without a
   // branch, so that a block's softmax and the next block's QK products form
-  // one straight-line region the compiler can interleave.  A block wholly
-  // after a wavefront's rows (causal) then gives p = 0 everywhere and leaves
-  // the state unchanged.
+  // one straight-line region the compiler can interleave.
   const int key_last = cmask ? (q < Sk - 1 ? q : Sk - 1) : Sk - 1;
 
   // Softmax of block j0's scores s (in place: s becomes the weights P) and the
@@ -285,16 +283,23 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_f32_kernel(
     // last read before the previous barrier.
     if (has2) load_k(j0 + 2 * BN, jb & 1);
     if (has1) load_v(j0 + BN, (jb + 1) & 1);
+    // Causal: a block whose first key comes after this wavefront's last row
+    // is skipped (it would only add zero weights); the loads above still run,
+    // the other wavefronts need them.
+    const bool cur_live = !cmask || j0 <= row0 + kRowsPerWave - 1;
+    const bool next_live = has1 && (!cmask || j0 + BN <= row0 + kRowsPerWave - 1);
     f32x16 s_next = f32x16{};
-    float f;
-    if (has1) {
-      s_next = qk((jb + 1) & 1);
-      f = softmax(s_cur, j0);
-    } else {
-      f = softmax(s_cur, j0);
+    if (cur_live) {
+      float f;
+      if (next_live) {
+        s_next = qk((jb + 1) & 1);
+        f = softmax(s_cur, j0);
+      } else {
+        f = softmax(s_cur, j0);
+      }
+      rescale(f);
+      pv(s_cur, jb & 1);
     }
-    rescale(f);
-    pv(s_cur, jb & 1);
     wait_vmem();
     __syncthreads();
     s_cur = s_next;
