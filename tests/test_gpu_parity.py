@@ -108,6 +108,25 @@ def test_gqa_prefill_bf16_full_size_sampled_rows(osx):
         check(got[b, h, rows], ref, "bf16", f"{w.name} b={b} h={h}")
 
 
+def test_prefill_bf16_long_sequence_sampled_rows(osx):
+    """A 2^20-token causal GQA prefill (bf16, d = 128, two query heads on one KV head): 8192 query tiles per head,
+    byte offsets 256x those of the benchmark workload; sampled rows (the first, tile and block edges, the middle,
+    the last) against the definition."""
+    S, D = 1 << 20, 128
+    print(f"case long prefill S={S}", flush=True)
+    t = synth.random_attn(21, "bf16", 1, 2, 1, S, S, D)
+    q, k, v = to_dev(t["q"]), to_dev(t["k"]), to_dev(t["v"])
+    out = torch.full_like(q, float("nan"))
+    osx.attn_fwd(q, k, v, causal=True, out=out)
+    torch.cuda.synchronize()
+    rows = sorted(set([0, 1, 63, 64, 127, 128, 4095, S // 2, S - 129, S - 128, S - 65, S - 64, S - 1]
+                      + np.random.default_rng(21).integers(0, S, 6).tolist()))
+    got = to_f64(out[:, :, rows])
+    for h in (0, 1):
+        ref = oracle.attention_rows(t["q"][0, h, rows], t["k"][0, 0], t["v"][0, 0], rows, causal=True, seq_q=S)
+        check(got[0, h], ref, "bf16", f"long prefill h={h}")
+
+
 def test_gqa_decode_bf16_full_size_sampled_heads(osx):
     w = synth.WORKLOADS["gqa_decode_bf16"]
     t = synth.attn_inputs(w)
