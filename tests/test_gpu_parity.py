@@ -127,6 +127,23 @@ def test_prefill_bf16_long_sequence_sampled_rows(osx):
         check(got[0, h], ref, "bf16", f"long prefill h={h}")
 
 
+def test_f32_long_sequence_sampled_rows(osx):
+    """fp32, one head of 2^17 queries and keys, d = 128, non-causal (1024 row tiles, no key split): sampled rows of
+    the plain and the normalised-output recurrence against the definition over all 131072 keys."""
+    S, D = 1 << 17, 128
+    print(f"case long fp32 S={S}", flush=True)
+    t = synth.random_attn(22, "f32", 1, 1, 1, S, S, D)
+    q, k, v = to_dev(t["q"]), to_dev(t["k"]), to_dev(t["v"])
+    rows = sorted(set([0, 1, 31, 32, 127, 128, S // 2, S - 33, S - 32, S - 1]
+                      + np.random.default_rng(22).integers(0, S, 6).tolist()))
+    ref = oracle.attention_rows(t["q"][0, 0, rows], t["k"][0, 0], t["v"][0, 0], rows)
+    for fn in (osx.attn_fwd, osx.attn_fwd_normalised):
+        out = torch.full_like(q, float("nan"))
+        fn(q, k, v, out=out)
+        torch.cuda.synchronize()
+        check(to_f64(out[0, 0, rows]), ref, "f32", f"long fp32 {fn.__name__}")
+
+
 def test_gqa_decode_bf16_full_size_sampled_heads(osx):
     w = synth.WORKLOADS["gqa_decode_bf16"]
     t = synth.attn_inputs(w)
