@@ -22,6 +22,11 @@
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *     asynchronously on it; nothing synchronises the device.  Buffers must stay
  *     alive until that work has finished.
+ *   - Alignment: the attention calls read and write 16-byte vectors, so q, k,
+ *     v, o and their workspace must be 16-byte aligned (lse 4-byte); the row
+ *     softmax calls need x and y aligned to their element size (2 or 4 bytes;
+ *     16-byte alignment selects the vector path) and a 4-byte aligned
+ *     workspace.  Anything else is OSX_EINVAL.
  *   - Arguments are checked on the host before anything is launched.  On error
  *     nothing is launched and a negative status is returned; osx_last_error()
  *     then describes the failure.  A call with no work (an empty batch, zero

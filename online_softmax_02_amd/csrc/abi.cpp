@@ -139,6 +139,9 @@ int plan_softmax(int64_t rows, int64_t cols, osx_plan* p) {
   return ok();
 }
 
+// True when p is not a multiple of `align` bytes.
+bool misaligned(const void* p, uintptr_t align) { return (reinterpret_cast<uintptr_t>(p) & (align - 1)) != 0; }
+
 bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   const char* pa = (const char*)a;
   const char* pb = (const char*)b;
@@ -179,10 +182,14 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, b
     return fail(OSX_EUNSUPPORTED, "the normalised-output recurrence is built for fp32 q, k, v and o only");
   if (p.kernel == OSX_KERNEL_NONE) return ok();
   if (!q || !k || !v || !o) return fail(OSX_EINVAL, "null q, k, v or o pointer");
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16))
+    return fail(OSX_EINVAL, "q, k, v and o must be 16-byte aligned (the kernels read and write 16-byte vectors)");
   if (want_lse && !lse) return fail(OSX_EINVAL, "null lse pointer");
+  if (lse && misaligned(lse, 4)) return fail(OSX_EINVAL, "lse must be 4-byte aligned");
   if (p.workspace_bytes > 0 && (!workspace || workspace_bytes < p.workspace_bytes))
     return fail(OSX_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : (size_t)0,
                 p.workspace_bytes);
+  if (p.workspace_bytes > 0 && misaligned(workspace, 16)) return fail(OSX_EINVAL, "workspace must be 16-byte aligned");
   if (!(scale > 0.0f) || !std::isfinite(scale)) scale = 1.0f / std::sqrt((float)head_dim);
   const size_t es = dtype == OSX_BF16 ? 2 : 4;
   const size_t nq = (size_t)batch * heads_q * seq_q * head_dim * es;
@@ -279,13 +286,16 @@ int softmax_rows(const void* x, void* y, int dtype, int64_t rows, int64_t cols, 
   if (st != OSX_OK) return st;
   if (p.kernel == OSX_KERNEL_NONE) return ok();
   if (!x || !y) return fail(OSX_EINVAL, "null x or y pointer");
-  const size_t n = (size_t)rows * (size_t)cols * (dtype == OSX_BF16 ? 2 : 4);
+  const uintptr_t es = dtype == OSX_BF16 ? 2 : 4;
+  if (misaligned(x, es) || misaligned(y, es)) return fail(OSX_EINVAL, "x and y must be aligned to their element size");
+  const size_t n = (size_t)rows * (size_t)cols * es;
   if (x != y && overlap(x, n, y, n)) return fail(OSX_EINVAL, "x and y overlap without being the same buffer");
   if (p.workspace_bytes > 0 && (!workspace || workspace_bytes < p.workspace_bytes))
     return fail(OSX_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : (size_t)0,
                 p.workspace_bytes);
   if (p.workspace_bytes > 0 && (overlap(workspace, p.workspace_bytes, x, n) || overlap(workspace, p.workspace_bytes, y, n)))
     return fail(OSX_EINVAL, "workspace overlaps x or y");
+  if (p.workspace_bytes > 0 && misaligned(workspace, 4)) return fail(OSX_EINVAL, "workspace must be 4-byte aligned");
   osx::SoftmaxArgs a;
   a.x = x;
   a.y = y;
@@ -378,6 +388,9 @@ int osx_attn_fwd_unfused(const void* q, const void* k, const void* v, void* o, i
   if (st != OSX_OK) return st;
   if (need == 0) return ok();
   if (!q || !k || !v || !o) return fail(OSX_EINVAL, "null q, k, v or o pointer");
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16))
+    return fail(OSX_EINVAL, "q, k, v and o must be 16-byte aligned (the kernels read and write 16-byte vectors)");
+  if (workspace && misaligned(workspace, 16)) return fail(OSX_EINVAL, "workspace must be 16-byte aligned");
   if (!workspace || workspace_bytes < need)
     return fail(OSX_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : (size_t)0,
                 need);
@@ -432,8 +445,10 @@ int osx_softmax_rows_3pass(const float* x, float* y, int64_t rows, int64_t cols,
   if (st != OSX_OK) return st;
   if (grid == 0) return ok();
   if (!x || !y) return fail(OSX_EINVAL, "null x or y pointer");
+  if (misaligned(x, 4) || misaligned(y, 4)) return fail(OSX_EINVAL, "x and y must be 4-byte aligned");
   const size_t n = (size_t)rows * (size_t)cols * sizeof(float);
   if (x != y && overlap(x, n, y, n)) return fail(OSX_EINVAL, "x and y overlap without being the same buffer");
+  if (workspace && misaligned(workspace, 4)) return fail(OSX_EINVAL, "workspace must be 4-byte aligned");
   if (!workspace || workspace_bytes < need)
     return fail(OSX_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : (size_t)0,
                 need);

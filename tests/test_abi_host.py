@@ -220,3 +220,27 @@ def test_read_probe_rejects_before_launch():
     assert lib.osx_read_probe(x, 1024, sink, need - 1, None) == osx.OSX_EWORKSPACE
     assert lib.osx_read_probe(x, 1 << 20, ctypes.c_void_p(0x100000 + 4096), need, None) == osx.OSX_EINVAL
     assert "overlap" in osx.last_error()
+
+
+def test_misaligned_pointers_are_rejected():
+    lib = osx.lib
+    a, b, c, o = (ctypes.c_void_p(x) for x in (0x100000, 0x200000, 0x300000, 0x400000))
+    off = ctypes.c_void_p(0x400000 + 2)  # a bf16 element past a 16-byte boundary
+    assert lib.osx_attn_fwd(a, b, c, off, BF16, 1, 4, 1, 16, 16, 128, 0, 0.0, None, 0, None) == osx.OSX_EINVAL
+    assert "aligned" in osx.last_error()
+    assert lib.osx_attn_fwd(ctypes.c_void_p(0x100008), b, c, o, F32, 1, 1, 1, 16, 16, 64, 0, 0.0, None, 0,
+                            None) == osx.OSX_EINVAL
+    assert lib.osx_attn_fwd_lse(a, b, c, o, ctypes.c_void_p(0x500002), F32, 1, 1, 1, 16, 16, 64, 0, 0.0, None, 0,
+                                None) == osx.OSX_EINVAL
+    need = osx.attn_fwd_workspace(F32, 1, 1, 1, 4096, 4096, 128)
+    assert lib.osx_attn_fwd(a, b, c, ctypes.c_void_p(0x10000000), F32, 1, 1, 1, 4096, 4096, 128, 0, 0.0,
+                            ctypes.c_void_p(0x20000004), need, None) == osx.OSX_EINVAL
+    assert lib.osx_attn_fwd_unfused(a, b, off, o, BF16, 1, 1, 1, 64, 64, 64, 0, 0.0, ctypes.c_void_p(0x900000),
+                                    1 << 20, None) == osx.OSX_EINVAL
+    x, y = ctypes.c_void_p(0x1000000), ctypes.c_void_p(0x2000000)
+    assert lib.osx_softmax_rows(ctypes.c_void_p(0x1000002), y, 2, 16, None, 0, None) == osx.OSX_EINVAL
+    assert lib.osx_softmax_rows_ex(x, ctypes.c_void_p(0x2000001), BF16, 2, 16, 0, 1.0, None, 0, None) == osx.OSX_EINVAL
+    assert lib.osx_softmax_rows_3pass(x, ctypes.c_void_p(0x2000002), 2, 1000, 1, None, 0, None) == osx.OSX_EINVAL
+    # the split kernels' workspace must be 4-byte aligned
+    assert lib.osx_softmax_rows(x, y, 1, 1 << 20, ctypes.c_void_p(0x3000002),
+                                osx.softmax_rows_workspace(1, 1 << 20), None) == osx.OSX_EINVAL

@@ -144,3 +144,30 @@ def test_softmax_options_defaults_equal_plain_softmax(osx):
     torch.cuda.synchronize()
     assert st == 0
     assert torch.equal(plain, ex)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("cols", [2048, 8192, 40000])
+def test_softmax_base_not_16_byte_aligned(osx, dtype, cols):
+    """x and y one element past a 16-byte boundary (column counts that would take the vector path): the scalar path
+    runs and matches the oracle, for each kernel (wavefront, workgroup, split)."""
+    rows = 3
+    print(f"case softmax offset base {dtype} {cols}", flush=True)
+    x = np.random.default_rng(cols).normal(0.0, 3.0, (rows, cols)).astype(np.float32)
+    if dtype == "bf16":
+        x = synth.round_to_bf16_bits(x)
+    xd = to_dev(x)
+    buf_x = torch.empty(rows * cols + 1, dtype=xd.dtype, device="cuda")
+    buf_y = torch.full_like(buf_x, float("nan"))
+    xs = buf_x[1:].view(rows, cols)
+    ys = buf_y[1:].view(rows, cols)
+    xs.copy_(xd)
+    assert xs.data_ptr() % 16 != 0
+    osx.softmax_rows(xs, out=ys, causal_period=rows, scale=0.5)
+    torch.cuda.synchronize()
+    got, ref = to_f64(ys), oracle.softmax_rows(x, causal_period=rows, scale=0.5)
+    err = np.abs(got - ref)
+    if dtype == "f32":
+        assert err.max() <= F32_ATOL, err.max()
+    else:
+        assert (err <= SOFTMAX_BF16_ATOL + SOFTMAX_BF16_RTOL * np.abs(ref)).all(), err.max()
