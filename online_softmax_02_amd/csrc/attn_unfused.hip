@@ -155,13 +155,15 @@ __global__ __launch_bounds__(kThreads) void scores_bf16_kernel(const uint16_t* _
 
 // ---- 3. O = P V -----------------------------------------------------------------
 // Workgroup: 128 queries of one head; wavefront w: queries 32w .. 32w + 31,
-// all D output columns (D / 32 accumulator tiles of O^T).  Per 64-key block the
-// workgroup stages V[64, D] in LDS (two buffers: the next block is loaded into
-// registers while the current one is multiplied) and each lane loads
-// P[q][k0 + 16 u + 8 hf .. + 7] (u = 0..3) as fp32 and rounds it to bf16 (the B
-// operand).  The A operand, V[k0 + 16 u + 8 hf .. + 7][d], comes from two
-// transposed LDS reads.  Keys past Sk: their V rows load as zero, so whatever
-// finite P the load returns there adds nothing.
+// all D output columns (D / 32 accumulator tiles of O^T).  Per 64-key block
+// the workgroup stages V[64, D] and P[128 queries, 64 keys] in LDS (two
+// buffers each: the next block is loaded into registers while the current one
+// is multiplied).  P is read from memory in whole 256-byte row segments (each
+// load instruction covers 4 rows), rounded to bf16 on the way into LDS, and
+// read back as the B operand P[q][k0 + 16 u + 8 hf .. + 7] (u = 0..3).  The A
+// operand, V[k0 + 16 u + 8 hf .. + 7][d], comes from two transposed LDS reads.
+// Keys past Sk: their V rows load as zero, so whatever finite P the load
+// returns there adds nothing.
 template <int D>
 struct PvTile {
   static constexpr int CH = D / 8;                // 16-byte chunks per V row
@@ -169,7 +171,15 @@ struct PvTile {
   static constexpr int ROW = D * 2;               // bytes per V row in LDS
   static constexpr int BLOCK_BYTES = kKeyBlock * ROW;
   static constexpr int CHUNKS = kKeyBlock * CH / kThreads;  // 16-byte chunks per thread per block
+  static constexpr int P_ROW = kKeyBlock * 2;     // bytes per bf16 P row in LDS (8 chunks of 8 keys)
+  static constexpr int P_BYTES = kRowsPerWg * P_ROW;
+  static constexpr int P_CHUNKS = kRowsPerWg * kKeyBlock / 4 / kThreads;  // fp32 16-byte chunks per thread
 };
+
+// P row swizzle: a B-operand read takes one 16-byte chunk from each of 32
+// consecutive 128-byte rows; XOR-ing the chunk index with (row / 2) % 8 spreads
+// each 16-row group over all the banks.
+__device__ __forceinline__ int p_swizzle(int row) { return (row >> 1) & 7; }
 
 // V row swizzle for the transposed reads: one ds_read_b64_tr_b16 serves 16 lanes
 // from 4 consecutive rows, 32 bytes of each; XOR-ing the chunk index with a
@@ -185,9 +195,12 @@ __global__ __launch_bounds__(kThreads) void pv_bf16_kernel(const float* __restri
                                                            int Hq, int Hkv, int Sq, int Sk) {
   using T = PvTile<D>;
   __shared__ __attribute__((aligned(16))) unsigned char lds_v[2][T::BLOCK_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_p[2][T::P_BYTES];
   const Head hd = head_of(Hq, Hkv);
   const int lane = threadIdx.x & 63, i = lane & 31, hf = lane >> 5;
-  const int q = hd.qb * kRowsPerWg + (threadIdx.x >> 6) * 32 + i;
+  const int wave = threadIdx.x >> 6;
+  const int q0 = hd.qb * kRowsPerWg;
+  const int q = q0 + wave * 32 + i;
   const __amdgpu_buffer_rsrc_t pr = make_rsrc(P + hd.q * (int64_t)Sq * Sk, (uint32_t)((int64_t)Sq * Sk * 4));
   const __amdgpu_buffer_rsrc_t vr = make_rsrc(V + hd.kv * Sk * D, (uint32_t)Sk * D * 2);
   const int nblk = (Sk + kKeyBlock - 1) / kKeyBlock;
@@ -208,15 +221,29 @@ __global__ __launch_bounds__(kThreads) void pv_bf16_kernel(const float* __restri
       *reinterpret_cast<u32x4*>(dst + row * T::ROW + ((ch ^ v_swizzle<T::CH>(row)) << 4)) = vst[n];
     }
   };
-  // P of one block: 4 k-steps x 8 keys, fp32.
-  f32x4 pf[4][2];
+  // P staging: fp32 chunk c = t + 256 n of the block is keys 4 (c % 16) .. + 3 of
+  // query row c / 16 (so each load instruction reads 4 whole 256-byte row
+  // segments); rounded to bf16, it fills half of LDS chunk (c % 16) / 2.
+  f32x4 pst[T::P_CHUNKS];
   auto load_p = [&](int kb) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint32_t off = (uint32_t)(((int64_t)q * Sk + kb * kKeyBlock + 16 * u + 8 * hf) * 4);
-      pf[u][0] = buf_ld16f(pr, off);
-      pf[u][1] = buf_ld16f(pr, off + 16);
+    for (int n = 0; n < T::P_CHUNKS; ++n) {
+      const int c = threadIdx.x + kThreads * n, row = c >> 4, ch = c & 15;
+      pst[n] = buf_ld16f(pr, (uint32_t)(((int64_t)(q0 + row) * Sk + kb * kKeyBlock + 4 * ch) * 4));
     }
+  };
+  auto store_p = [&](unsigned char* dst) {
+#pragma unroll
+    for (int n = 0; n < T::P_CHUNKS; ++n) {
+      const int c = threadIdx.x + kThreads * n, row = c >> 4, ch = c & 15;
+      const u32x2 w = {pack_bf16x2(pst[n].x, pst[n].y), pack_bf16x2(pst[n].z, pst[n].w)};
+      *reinterpret_cast<u32x2*>(dst + row * T::P_ROW + ((((ch >> 1) ^ p_swizzle(row)) << 4) | ((ch & 1) << 3))) = w;
+    }
+  };
+  // B operand of step u: P[q][16 u + 8 hf .. + 7] of this wavefront's row i.
+  auto p_frag = [&](const unsigned char* buf, int u) -> bf16x8 {
+    const int row = wave * 32 + i;
+    return *reinterpret_cast<const bf16x8*>(buf + row * T::P_ROW + (((2 * u + hf) ^ p_swizzle(row)) << 4));
   };
   // Transposed V read: in each 16-lane group, lane s addresses row base + s / 4,
   // columns c0 + 4 (s % 4) .. + 3; lane s then receives column c0 + s of those
@@ -241,14 +268,11 @@ __global__ __launch_bounds__(kThreads) void pv_bf16_kernel(const float* __restri
   load_v(0);
   load_p(0);
   store_v(lds_v[0]);
+  store_p(lds_p[0]);
   __syncthreads();
   for (int kb = 0; kb < nblk; ++kb) {
-    const unsigned char* cur = lds_v[kb & 1];
-    bf16x8 pb[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      pb[u] = pack_bf16x8(pf[u][0].x, pf[u][0].y, pf[u][0].z, pf[u][0].w, pf[u][1].x, pf[u][1].y, pf[u][1].z,
-                          pf[u][1].w);
+    const unsigned char* cur_v = lds_v[kb & 1];
+    const unsigned char* cur_p = lds_p[kb & 1];
     const bool more = kb + 1 < nblk;
     if (more) {
       load_v(kb + 1);
@@ -256,11 +280,15 @@ __global__ __launch_bounds__(kThreads) void pv_bf16_kernel(const float* __restri
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
+      const bf16x8 pb = p_frag(cur_p, u);
 #pragma unroll
       for (int dt = 0; dt < T::DT; ++dt)
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag(cur, u, dt), pb[u], acc[dt], 0, 0, 0);
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag(cur_v, u, dt), pb, acc[dt], 0, 0, 0);
     }
-    if (more) store_v(lds_v[(kb + 1) & 1]);
+    if (more) {
+      store_v(lds_v[(kb + 1) & 1]);
+      store_p(lds_p[(kb + 1) & 1]);
+    }
     __syncthreads();
   }
   if (q >= Sq) return;
