@@ -244,3 +244,12 @@ def test_misaligned_pointers_are_rejected():
     # the split kernels' workspace must be 4-byte aligned
     assert lib.osx_softmax_rows(x, y, 1, 1 << 20, ctypes.c_void_p(0x3000002),
                                 osx.softmax_rows_workspace(1, 1 << 20), None) == osx.OSX_EINVAL
+
+
+def test_non_finite_softmax_scale_is_rejected():
+    """The host checks keep IEEE semantics: a NaN or infinite logit scale is an error, not a silent pass."""
+    lib = osx.lib
+    x, y = ctypes.c_void_p(0x1000000), ctypes.c_void_p(0x2000000)
+    for bad in (float("nan"), float("inf"), -1.0, 0.0):
+        assert lib.osx_softmax_rows_ex(x, y, F32, 2, 16, 0, bad, None, 0, None) == osx.OSX_EINVAL
+        assert "scale" in osx.last_error()
