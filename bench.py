@@ -21,7 +21,7 @@ copied to HBM before timing.  Durations come from one HIP event pair recorded
 on the stream the kernels run on, around the whole timed region of
 back-to-back calls, divided by the number of calls.
 
-``--gpus N`` with N > 1 exits: this build runs on one GPU.
+``--gpus N`` with N > 1 exits: the library and this benchmark use one GPU.
 Prints one JSON line on stdout.
 """
 import argparse
@@ -347,7 +347,7 @@ def cpu_baseline(t, w, seconds):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} requested; this build runs on exactly one GPU "
+        print(f"bench.py: --gpus {args.gpus} requested; the library and this benchmark use exactly one GPU "
               "(no collectives or sharding). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
