@@ -31,6 +31,9 @@
  *     nothing is launched and a negative status is returned; osx_last_error()
  *     then describes the failure.  A call with no work (an empty batch, zero
  *     query rows, zero rows or columns) returns OSX_OK and launches nothing.
+ *   - With OSX_LOG=1 in the environment (read once per process) every call of
+ *     osx_attn_fwd* and osx_softmax_rows* that launches work prints one line on
+ *     stderr: the problem and the kernel, grid and workspace the plan chose.
  */
 #ifndef OSX_H
 #define OSX_H
@@ -86,7 +89,11 @@ typedef struct osx_plan {
  * causal != 0 keeps key j for query i only when j <= i, and only when
  * seq_q > 1 (the eager reference of section 自注意力原理 skips the mask for a
  * single query row); with seq_q > 1 it requires seq_q == seq_k.
- * Supported head_dim: fp32 any multiple of 4 in [4, 128]; bf16 64 or 128.
+ * Supported head_dim: fp32 any multiple of 4 in [4, 128]; bf16 any multiple of
+ * 16 in [16, 128].  Head dims that are not a multiple of the kernel's tile
+ * width (32 for fp32; 64 or 128 for bf16) run with the missing columns read as
+ * zeros and never stored (page "softmax_attention", section 实现思路, pads the
+ * head dimension up to the block width and masks the padded lanes).
  * Returns OSX_OK, OSX_EINVAL or OSX_EUNSUPPORTED; `out` may be NULL.
  */
 int osx_attn_plan(int dtype, int batch, int heads_q, int heads_kv, int seq_q, int seq_k, int head_dim, int causal,
@@ -100,6 +107,17 @@ int osx_attn_plan(int dtype, int batch, int heads_q, int heads_kv, int seq_q, in
  */
 int osx_attn_fwd_workspace(int dtype, int batch, int heads_q, int heads_kv, int seq_q, int seq_k, int head_dim,
                            int causal, size_t* bytes);
+
+/*
+ * The same size as a return value: the bytes of caller-allocated scratch
+ * osx_attn_fwd needs for this problem (page "Softmax 算子的实现与优化", section
+ * Baseline: the host allocates the scratch buffers the kernels combine
+ * through).  0 when none is needed -- and also for a problem osx_attn_fwd
+ * would reject (the reason is then in osx_last_error(); osx_attn_plan returns
+ * the status).
+ */
+size_t osx_attn_fwd_workspace_bytes(int dtype, int batch, int heads_q, int heads_kv, int seq_q, int seq_k,
+                                    int head_dim, int causal);
 
 /*
  * osx_attn_fwd -- single-pass attention forward.
@@ -167,7 +185,8 @@ int osx_attn_fwd_normalised(const void* q, const void* k, const void* v, void* o
  *   3. O = P V, with P rounded to bf16 for the products (fp32 accumulation).
  * All keys are multiplied, masked ones included, as on the page.
  *
- * dtype must be OSX_BF16 (else OSX_EUNSUPPORTED); head_dim 64 or 128;
+ * dtype must be OSX_BF16 (else OSX_EUNSUPPORTED); head_dim 64 or 128 (others
+ * OSX_EUNSUPPORTED);
  * seq_q * seq_k at most 2^29 (OSX_EUNSUPPORTED above).  Layouts, GQA, causal
  * and scale as osx_attn_fwd.  workspace: osx_attn_fwd_unfused_workspace bytes
  * (the score matrix, 4 bytes per score, plus the softmax's own workspace);
@@ -184,6 +203,14 @@ int osx_softmax_rows_plan(int64_t rows, int64_t cols, osx_plan* out);
 
 /* Workspace bytes osx_softmax_rows needs for x[rows, cols] (0 unless rows are split), via *bytes. */
 int osx_softmax_rows_workspace(int64_t rows, int64_t cols, size_t* bytes);
+
+/*
+ * The same size as a return value (page "Softmax 算子的实现与优化", section
+ * Baseline: the caller allocates the scratch that per-chunk partials are
+ * merged through).  0 when none is needed, and for a shape osx_softmax_rows
+ * would reject (negative sizes, cols == 0 with rows > 0).
+ */
+size_t osx_softmax_rows_workspace_bytes(int64_t rows, int64_t cols);
 
 /*
  * osx_softmax_rows -- y[r, :] = exp(x[r, :] - m_r) / l_r for every row r, with

@@ -56,11 +56,15 @@ def _load() -> ctypes.CDLL:
     attn_shape = [_i, _i, _i, _i, _i, _i, _i, _i]  # dtype, B, Hq, Hkv, Sq, Sk, D, causal
     lib.osx_attn_plan.argtypes = attn_shape + [ctypes.POINTER(Plan)]
     lib.osx_attn_fwd_workspace.argtypes = attn_shape + [ctypes.POINTER(_sz)]
+    lib.osx_attn_fwd_workspace_bytes.argtypes = attn_shape
+    lib.osx_attn_fwd_workspace_bytes.restype = _sz
     lib.osx_attn_fwd.argtypes = [_vp, _vp, _vp, _vp] + attn_shape + [_f, _vp, _sz, _vp]
     lib.osx_attn_fwd_lse.argtypes = [_vp, _vp, _vp, _vp, _vp] + attn_shape + [_f, _vp, _sz, _vp]
     lib.osx_attn_fwd_normalised.argtypes = [_vp, _vp, _vp, _vp, _vp] + attn_shape + [_f, _vp, _sz, _vp]
     lib.osx_softmax_rows_plan.argtypes = [_i64, _i64, ctypes.POINTER(Plan)]
     lib.osx_softmax_rows_workspace.argtypes = [_i64, _i64, ctypes.POINTER(_sz)]
+    lib.osx_softmax_rows_workspace_bytes.argtypes = [_i64, _i64]
+    lib.osx_softmax_rows_workspace_bytes.restype = _sz
     lib.osx_softmax_rows.argtypes = [_vp, _vp, _i64, _i64, _vp, _sz, _vp]
     lib.osx_softmax_rows_ex.argtypes = [_vp, _vp, _i, _i64, _i64, _i64, _f, _vp, _sz, _vp]
     lib.osx_attn_fwd_unfused_workspace.argtypes = attn_shape + [ctypes.POINTER(_sz)]
@@ -145,6 +149,32 @@ def _stream(t, stream):
     return _vp(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
+def _workspace(need: int, workspace, device):
+    """The workspace tensor to pass (the caller's, or a new one when `need` > 0 and none was given), its pointer and
+    its length in bytes.  The caller of this helper keeps the returned tensor referenced until the launch is
+    enqueued, and hands it to _hold() afterwards."""
+    torch = _torch()
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    if workspace is None:
+        return None, None, 0
+    return workspace, workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def _hold(ws, stream) -> None:
+    """Keep a workspace the binding allocated from being reused before the kernels on `stream` are done with it.
+
+    torch's caching allocator hands freed memory to later allocations in the order of the current stream; work
+    launched on another stream is ordered only once the tensor is recorded on that stream."""
+    if ws is None or stream is None:
+        return
+    torch = _torch()
+    s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(
+        stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream), device=ws.device)
+    if s.cuda_stream != torch.cuda.current_stream(ws.device).cuda_stream:
+        ws.record_stream(s)
+
+
 def _dtype_code(t) -> int:
     torch = _torch()
     if t.dtype == torch.float32:
@@ -179,11 +209,8 @@ def _attn_prepare(q, k, v, causal, out, workspace):
     elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
         raise ValueError("out must be a contiguous tensor like q")
     need = attn_fwd_workspace(code, B, Hq, Hkv, Sq, Sk, D, causal)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    return squeeze, q, k, v, out, code, (B, Hq, Hkv, Sq, Sk, D), ws_ptr, ws_len
+    ws = _workspace(need, workspace, q.device)
+    return squeeze, q, k, v, out, code, (B, Hq, Hkv, Sq, Sk, D), ws
 
 
 def _lse_tensor(q, shape, lse):
@@ -206,15 +233,17 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None
     ``return_lse`` also the float32 [B, Hq, Sq] (or [M]) log-sum-exp of each
     row's scaled, masked scores (``lse`` may supply that tensor).
     """
-    squeeze, q, k, v, out, code, shape, ws_ptr, ws_len = _attn_prepare(q, k, v, causal, out, workspace)
+    squeeze, q, k, v, out, code, shape, (ws, ws_ptr, ws_len) = _attn_prepare(q, k, v, causal, out, workspace)
     sc = float(scale) if scale else 0.0
     if not (return_lse or lse is not None):
         _check(lib.osx_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), code, *shape, int(causal),
                                 sc, ws_ptr, ws_len, _stream(q, stream)))
+        _hold(ws if workspace is None else None, stream)
         return out[0, 0] if squeeze else out
     lse = _lse_tensor(q, shape, lse)
     _check(lib.osx_attn_fwd_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), code, *shape,
                                 int(causal), sc, ws_ptr, ws_len, _stream(q, stream)))
+    _hold(ws if workspace is None else None, stream)
     if squeeze:
         return out[0, 0], lse.reshape(-1)
     return out, lse
@@ -223,7 +252,7 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None
 def attn_fwd_normalised(q, k, v, causal: bool = False, scale: float | None = None, out=None, workspace=None,
                         stream=None, return_lse: bool = False, lse=None):
     """attn_fwd computed with the normalised-output recurrence (osx_attn_fwd_normalised): float32 only."""
-    squeeze, q, k, v, out, code, shape, ws_ptr, ws_len = _attn_prepare(q, k, v, causal, out, workspace)
+    squeeze, q, k, v, out, code, shape, (ws, ws_ptr, ws_len) = _attn_prepare(q, k, v, causal, out, workspace)
     sc = float(scale) if scale else 0.0
     want = return_lse or lse is not None
     if want:
@@ -231,6 +260,7 @@ def attn_fwd_normalised(q, k, v, causal: bool = False, scale: float | None = Non
     _check(lib.osx_attn_fwd_normalised(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                        lse.data_ptr() if want else None, code, *shape, int(causal), sc, ws_ptr, ws_len,
                                        _stream(q, stream)))
+    _hold(ws if workspace is None else None, stream)
     o = out[0, 0] if squeeze else out
     if not want:
         return o
@@ -253,16 +283,13 @@ def softmax_rows(x, out=None, workspace=None, stream=None, causal_period: int = 
         out = torch.empty_like(x)
     elif out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous():
         raise ValueError("out must be a contiguous tensor like x")
-    need = softmax_rows_workspace(rows, cols)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ws, ws_ptr, ws_len = _workspace(softmax_rows_workspace(rows, cols), workspace, x.device)
     if x.dtype == torch.float32 and not causal_period and scale == 1.0:
         _check(lib.osx_softmax_rows(x.data_ptr(), out.data_ptr(), rows, cols, ws_ptr, ws_len, _stream(x, stream)))
     else:
         _check(lib.osx_softmax_rows_ex(x.data_ptr(), out.data_ptr(), _dtype_code(x), rows, cols, int(causal_period),
                                        float(scale), ws_ptr, ws_len, _stream(x, stream)))
+    _hold(ws if workspace is None else None, stream)
     return out
 
 
@@ -295,14 +322,12 @@ def attn_fwd_unfused(q, k, v, causal: bool = False, scale: float | None = None, 
         out = torch.empty_like(q)
     elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
         raise ValueError("out must be a contiguous tensor like q")
-    need = attn_fwd_unfused_workspace(code, B, Hq, Hkv, Sq, Sk, D, causal)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ws, ws_ptr, ws_len = _workspace(attn_fwd_unfused_workspace(code, B, Hq, Hkv, Sq, Sk, D, causal), workspace,
+                                    q.device)
     _check(lib.osx_attn_fwd_unfused(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), code, B, Hq, Hkv, Sq,
                                     Sk, D, int(causal), float(scale) if scale else 0.0, ws_ptr, ws_len,
                                     _stream(q, stream)))
+    _hold(ws if workspace is None else None, stream)
     return out[0, 0] if squeeze else out
 
 
@@ -328,13 +353,10 @@ def softmax_rows_3pass(x, method: int, out=None, workspace=None, stream=None):
         out = torch.empty_like(x)
     elif out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous():
         raise ValueError("out must be a contiguous tensor like x")
-    need = softmax_rows_3pass_workspace(rows, cols, method)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ws, ws_ptr, ws_len = _workspace(softmax_rows_3pass_workspace(rows, cols, method), workspace, x.device)
     _check(lib.osx_softmax_rows_3pass(x.data_ptr(), out.data_ptr(), rows, cols, method, ws_ptr, ws_len,
                                       _stream(x, stream)))
+    _hold(ws if workspace is None else None, stream)
     return out
 
 

@@ -2,9 +2,11 @@
 // allocated here and nothing synchronises the device.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "launch.hpp"
@@ -13,6 +15,36 @@
 namespace {
 
 thread_local char g_err[512] = "";
+
+// OSX_LOG=1 in the environment: one line on stderr per launching call, naming
+// the kernel the plan chose (read once per process).
+bool log_enabled() {
+  static const bool on = [] {
+    const char* v = std::getenv("OSX_LOG");
+    return v && v[0] && std::strcmp(v, "0") != 0;
+  }();
+  return on;
+}
+
+const char* kernel_name(int k) {
+  switch (k) {
+    case OSX_KERNEL_NONE: return "none";
+    case OSX_KERNEL_PREFILL_F32: return "prefill_f32";
+    case OSX_KERNEL_PREFILL_BF16: return "prefill_bf16";
+    case OSX_KERNEL_DECODE_BF16: return "decode_bf16";
+    case OSX_KERNEL_SOFTMAX_ROW: return "softmax_row";
+    case OSX_KERNEL_SOFTMAX_SPLIT: return "softmax_split";
+    case OSX_KERNEL_SOFTMAX_WAVE: return "softmax_wave";
+    default: return "?";
+  }
+}
+
+void log_plan(const char* call, const osx_plan& p, const char* shape) {
+  if (!log_enabled()) return;
+  std::fprintf(stderr, "osx: %s %s -> %s grid=%lld threads=%d block_m=%d splits=%d heads_per_wg=%d workspace=%zu\n",
+               call, shape, kernel_name(p.kernel), (long long)p.grid, p.threads, p.block_m, p.splits, p.heads_per_wg,
+               p.workspace_bytes);
+}
 
 int fail(int status, const char* fmt, ...) {
   va_list ap;
@@ -47,8 +79,8 @@ int plan_attn(int dtype, int batch, int heads_q, int heads_kv, int seq_q, int se
   if (head_dim == 0) return fail(OSX_EINVAL, "head_dim == 0");
   if (dtype == OSX_F32 && (head_dim % 4 != 0 || head_dim > 128))
     return fail(OSX_EUNSUPPORTED, "fp32 head_dim %d: must be a multiple of 4 and at most 128", head_dim);
-  if (dtype == OSX_BF16 && head_dim != 64 && head_dim != 128)
-    return fail(OSX_EUNSUPPORTED, "bf16 head_dim %d: must be 64 or 128", head_dim);
+  if (dtype == OSX_BF16 && (head_dim % 16 != 0 || head_dim > 128))
+    return fail(OSX_EUNSUPPORTED, "bf16 head_dim %d: must be a multiple of 16 and at most 128", head_dim);
   // The kernels address one head's Q, K, V or O through 32-bit buffer ranges and
   // 32-bit element offsets: each must stay below 2^31 bytes.
   {
@@ -150,6 +182,32 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 
 }  // namespace
 
+namespace osx {
+
+hipError_t device_cu_count(int* n_cu) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];  // 0 = not looked up yet
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int n = cache[dev].load(std::memory_order_relaxed);
+    if (n > 0) {
+      *n_cu = n;
+      return hipSuccess;
+    }
+  }
+  int n = 0;
+  e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (n <= 0) return hipErrorInvalidDevice;
+  if (dev >= 0 && dev < kMaxDevices) cache[dev].store(n, std::memory_order_relaxed);
+  *n_cu = n;
+  return hipSuccess;
+}
+
+}  // namespace osx
+
 extern "C" {
 
 int osx_attn_plan(int dtype, int batch, int heads_q, int heads_kv, int seq_q, int seq_k, int head_dim, int causal,
@@ -166,6 +224,13 @@ int osx_attn_fwd_workspace(int dtype, int batch, int heads_q, int heads_kv, int 
   int st = plan_attn(dtype, batch, heads_q, heads_kv, seq_q, seq_k, head_dim, causal, &p);
   if (bytes) *bytes = st == OSX_OK ? p.workspace_bytes : 0;
   return st;
+}
+
+size_t osx_attn_fwd_workspace_bytes(int dtype, int batch, int heads_q, int heads_kv, int seq_q, int seq_k,
+                                    int head_dim, int causal) {
+  osx_plan p;
+  return plan_attn(dtype, batch, heads_q, heads_kv, seq_q, seq_k, head_dim, causal, &p) == OSX_OK ? p.workspace_bytes
+                                                                                                : 0;
 }
 
 }  // extern "C"
@@ -191,6 +256,13 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, b
                 p.workspace_bytes);
   if (p.workspace_bytes > 0 && misaligned(workspace, 16)) return fail(OSX_EINVAL, "workspace must be 16-byte aligned");
   if (!(scale > 0.0f) || !std::isfinite(scale)) scale = 1.0f / std::sqrt((float)head_dim);
+  if (log_enabled()) {
+    char shape[160];
+    std::snprintf(shape, sizeof shape, "%s B=%d Hq=%d Hkv=%d Sq=%d Sk=%d d=%d causal=%d%s%s",
+                  dtype == OSX_BF16 ? "bf16" : "f32", batch, heads_q, heads_kv, seq_q, seq_k, head_dim, causal ? 1 : 0,
+                  want_lse || lse ? " lse" : "", normalised ? " normalised" : "");
+    log_plan("attn_fwd", p, shape);
+  }
   const size_t es = dtype == OSX_BF16 ? 2 : 4;
   const size_t nq = (size_t)batch * heads_q * seq_q * head_dim * es;
   const size_t nkv = (size_t)batch * heads_kv * seq_k * head_dim * es;
@@ -272,6 +344,11 @@ int osx_softmax_rows_workspace(int64_t rows, int64_t cols, size_t* bytes) {
   return st;
 }
 
+size_t osx_softmax_rows_workspace_bytes(int64_t rows, int64_t cols) {
+  osx_plan p;
+  return plan_softmax(rows, cols, &p) == OSX_OK ? p.workspace_bytes : 0;
+}
+
 }  // extern "C"
 
 namespace {
@@ -296,6 +373,13 @@ int softmax_rows(const void* x, void* y, int dtype, int64_t rows, int64_t cols, 
   if (p.workspace_bytes > 0 && (overlap(workspace, p.workspace_bytes, x, n) || overlap(workspace, p.workspace_bytes, y, n)))
     return fail(OSX_EINVAL, "workspace overlaps x or y");
   if (p.workspace_bytes > 0 && misaligned(workspace, 4)) return fail(OSX_EINVAL, "workspace must be 4-byte aligned");
+  if (log_enabled()) {
+    char shape[128];
+    std::snprintf(shape, sizeof shape, "%s rows=%lld cols=%lld causal_period=%lld%s",
+                  dtype == OSX_BF16 ? "bf16" : "f32", (long long)rows, (long long)cols, (long long)causal_period,
+                  x == y ? " in-place" : "");
+    log_plan("softmax_rows", p, shape);
+  }
   osx::SoftmaxArgs a;
   a.x = x;
   a.y = y;
@@ -343,6 +427,8 @@ int plan_unfused(int dtype, int batch, int heads_q, int heads_kv, int seq_q, int
   if (st != OSX_OK) return st;
   if (p.kernel == OSX_KERNEL_NONE) return ok();
   if (dtype != OSX_BF16) return fail(OSX_EUNSUPPORTED, "unfused attention takes bf16 q, k, v, o");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(OSX_EUNSUPPORTED, "unfused attention: head_dim %d, must be 64 or 128", head_dim);
   if ((int64_t)batch * heads_q > 65535)
     return fail(OSX_EUNSUPPORTED, "unfused attention: batch * heads_q = %lld exceeds 65535",
                 (long long)batch * heads_q);

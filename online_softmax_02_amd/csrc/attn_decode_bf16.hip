@@ -12,6 +12,11 @@
 //    two workgroups per CU.  K feeds S^T = K Q^T directly from registers; V is written
 //    to the wavefront's LDS slice transposed (keys permuted so each lane's 8
 //    keys are one 16-byte read) and feeds O^T += V^T P^T.
+//  * A head dimension d that is a multiple of 16 and not 64 or 128 runs in
+//    the 64- or 128-wide kernel: padded columns of Q, K and V read as zeros
+//    (their loads go to an offset past the buffer range), add nothing to the
+//    scores and are never stored (page "softmax_attention", section 实现思路,
+//    pads d up to the block width and masks the extra lanes).
 //  * The 4 wavefront states are merged in LDS.  With one split that state is
 //    final and the workgroup writes O = acc / l itself; otherwise it writes
 //    one partial (m, l, acc) per split and a second kernel merges the splits
@@ -26,6 +31,7 @@ namespace {
 
 constexpr int BN = kDecodeBlockN;  // 32 keys per wavefront step
 constexpr int NCOL = 16;           // MFMA columns available for query heads
+constexpr uint32_t kOffNowhere = 0x80000000u;  // a buffer offset past any head (heads are < 2^31 bytes)
 
 template <int D>
 struct DecTile {
@@ -53,33 +59,42 @@ struct Regs {
 };
 
 // Keys past the split's end (and so past Sk) read as zeros through the buffer
-// range; the score mask removes them (their weights are exactly 0).
+// range; the score mask removes them (their weights are exactly 0).  Global
+// rows are d elements long; columns d .. D-1 (padding) read as zeros.
 template <int D>
 __device__ __forceinline__ void load_regs(Regs<D>& R, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr, int j0,
-                                          int lane) {
+                                          int lane, int d) {
   using T = DecTile<D>;
   const int l16 = lane & 15, grp = lane >> 4;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int j = j0 + 16 * t + l16;
 #pragma unroll
-    for (int kc = 0; kc < T::KC; ++kc) R.k[t][kc] = ld16_nt(kr, (uint32_t)(j * D + 32 * kc + 8 * grp) * 2);
+    for (int kc = 0; kc < T::KC; ++kc) {
+      const int col = 32 * kc + 8 * grp;
+      R.k[t][kc] = ld16_nt(kr, col < d ? (uint32_t)(j * d + col) * 2 : kOffNowhere);
+    }
   }
 #pragma unroll
   for (int r = 0; r < T::VU; ++r) {
     const int u = lane + kWaveSize * r;
     const int kq = u / T::CH, ch = u % T::CH;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) R.v[r][jj] = ld16_nt(vr, (uint32_t)((j0 + 4 * kq + jj) * D + 8 * ch) * 2);
+    for (int jj = 0; jj < 4; ++jj)
+      R.v[r][jj] = ld16_nt(vr, 8 * ch < d ? (uint32_t)((j0 + 4 * kq + jj) * d + 8 * ch) * 2 : kOffNowhere);
   }
 }
 
-template <int D>
+// D: the kernel's (padded) head dimension, 64 or 128.  PAD: the true head
+// dimension d_arg (a multiple of 16, at most D) is smaller; global rows, the
+// output and the partial states are d_arg elements long.
+template <int D, bool PAD>
 __global__ __launch_bounds__(kAttnThreads, 2) void decode_bf16_kernel(
     const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, const uint16_t* __restrict__ Vg,
-    float* __restrict__ ws, uint16_t* __restrict__ Og, float* __restrict__ Lse, int Hq, int Hkv, int Sk, float c,
-    int splits, int keys_per_split) {
+    float* __restrict__ ws, uint16_t* __restrict__ Og, float* __restrict__ Lse, int Hq, int Hkv, int Sk, int d_arg,
+    float c, int splits, int keys_per_split) {
   using T = DecTile<D>;
+  const int d = PAD ? d_arg : D;
   // V^T slices during the stream; reused for the wavefront merge afterwards.
   constexpr int MERGE_BYTES = kAttnWaves * NCOL * (D + 2) * 4;
   constexpr int LDS_BYTES = kAttnWaves * T::VT_BYTES > MERGE_BYTES ? kAttnWaves * T::VT_BYTES : MERGE_BYTES;
@@ -108,17 +123,18 @@ __global__ __launch_bounds__(kAttnThreads, 2) void decode_bf16_kernel(
   // without touching memory, so the stream below can prefetch one block past
   // its end unconditionally (those keys are masked).
   const int k_lim = k_end > k_begin ? k_end : k_begin;
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc(Kg + (size_t)bkv * Sk * D, (uint32_t)k_lim * D * 2);
-  const __amdgpu_buffer_rsrc_t vr = make_rsrc(Vg + (size_t)bkv * Sk * D, (uint32_t)k_lim * D * 2);
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(Kg + (size_t)bkv * Sk * d, (uint32_t)k_lim * d * 2);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(Vg + (size_t)bkv * Sk * d, (uint32_t)k_lim * d * 2);
 
   // Q^T as the B operand: column l16 is query head kvh*G + l16 (zero past G).
   bf16x8 qop[T::KC];
   {
     const int hq = kvh * G + (l16 < G ? l16 : 0);
-    const uint16_t* qp = Qg + (size_t)(b * Hq + hq) * D;
+    const uint16_t* qp = Qg + (size_t)(b * Hq + hq) * d;
 #pragma unroll
     for (int kc = 0; kc < T::KC; ++kc) {
-      u32x4 x = ld16(qp + 32 * kc + 8 * grp);
+      const int col = 32 * kc + 8 * grp;
+      u32x4 x = col < d ? ld16(qp + col) : u32x4{0u, 0u, 0u, 0u};
       if (l16 >= G) x = u32x4{0u, 0u, 0u, 0u};
       qop[kc] = __builtin_bit_cast(bf16x8, x);
     }
@@ -214,12 +230,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void decode_bf16_kernel(
   int j0 = k_begin + BN * wave;
   const int nblk = j0 < k_end ? (k_end - j0 + kStep - 1) / kStep : 0;
   Regs<D> ra, rb;
-  load_regs<D>(ra, kr, vr, j0, lane);
+  load_regs<D>(ra, kr, vr, j0, lane, d);
   for (int pair = 0; pair < nblk / 2; ++pair) {
-    load_regs<D>(rb, kr, vr, j0 + kStep, lane);
+    load_regs<D>(rb, kr, vr, j0 + kStep, lane, d);
     __builtin_amdgcn_sched_barrier(0);
     compute(ra, j0);
-    load_regs<D>(ra, kr, vr, j0 + 2 * kStep, lane);
+    load_regs<D>(ra, kr, vr, j0 + 2 * kStep, lane, d);
     __builtin_amdgcn_sched_barrier(0);
     compute(rb, j0 + kStep);
     j0 += 2 * kStep;
@@ -246,8 +262,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void decode_bf16_kernel(
   const size_t n_part = (size_t)gridDim.x * G;
   float* ws_acc = ws + 2 * n_part;
   const size_t part0 = (size_t)wg * G;
-  for (int idx = tid; idx < G * D; idx += kAttnThreads) {
-    const int col = idx / D, dd = idx % D;
+  for (int idx = tid; idx < G * d; idx += kAttnThreads) {
+    const int col = idx / d, dd = idx % d;
     float M = kNegInf;
 #pragma unroll
     for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, ml[(w * NCOL + col) * 2]);
@@ -264,11 +280,11 @@ __global__ __launch_bounds__(kAttnThreads, 2) void decode_bf16_kernel(
       // The workgroup saw every key: its merged state is final, O = acc / l.
       // (Every key split holds at least one key, so l > 0.)
       const size_t bh = (size_t)b * Hq + kvh * G + col;
-      Og[bh * D + dd] = (uint16_t)(pack_bf16x2(asum / lsum, 0.f) & 0xffffu);
+      Og[bh * d + dd] = (uint16_t)(pack_bf16x2(asum / lsum, 0.f) & 0xffffu);
       // log sum_j exp(scale * s_j) = ln 2 * (M + log2 l), M in the log2 domain
       if (Lse && dd == 0) Lse[bh] = (M + log2f(lsum)) * kLn2;
     } else {
-      ws_acc[(part0 + col) * D + dd] = asum;
+      ws_acc[(part0 + col) * d + dd] = asum;
       if (dd == 0) {
         ws_ml[(part0 + col) * 2] = M;
         ws_ml[(part0 + col) * 2 + 1] = lsum;
@@ -278,10 +294,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void decode_bf16_kernel(
 }
 
 // Merge the splits of one (batch, query head): O = sum acc_s 2^(m_s-m) / sum l_s 2^(m_s-m).
-template <int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restrict__ ws, uint16_t* __restrict__ Og,
-                                                           float* __restrict__ Lse, int Hq, int Hkv, int splits,
-                                                           int n_wg) {
+// One thread per output column: the launch has d threads.
+__global__ __launch_bounds__(128) void decode_combine_kernel(const float* __restrict__ ws, uint16_t* __restrict__ Og,
+                                                             float* __restrict__ Lse, int Hq, int Hkv, int splits,
+                                                             int n_wg, int D) {
   const int bh = blockIdx.x;
   const int b = bh / Hq, hq = bh % Hq;
   const int G = Hq / Hkv;
@@ -328,31 +344,31 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restri
   Og[(size_t)bh * D + dd] = (uint16_t)(w & 0xffffu);
 }
 
-template <int D>
+template <int D, bool PAD>
 hipError_t launch(const AttnArgs& a) {
   const int splits = a.plan.splits;
   int kps = (a.seq_k + splits - 1) / splits;
   kps = (kps + BN - 1) / BN * BN;
   float* ws = static_cast<float*>(a.workspace);
-  hipLaunchKernelGGL(decode_bf16_kernel<D>, dim3((unsigned)a.plan.grid), dim3(kAttnThreads), 0, a.stream,
+  hipLaunchKernelGGL((decode_bf16_kernel<D, PAD>), dim3((unsigned)a.plan.grid), dim3(kAttnThreads), 0, a.stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), ws, static_cast<uint16_t*>(a.o), a.lse, a.heads_q, a.heads_kv,
-                     a.seq_k, a.c, splits, kps);
+                     a.seq_k, a.head_dim, a.c, splits, kps);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
-  hipLaunchKernelGGL(decode_combine_kernel<D>, dim3((unsigned)(a.batch * a.heads_q)), dim3(D), 0, a.stream, ws,
-                     static_cast<uint16_t*>(a.o), a.lse, a.heads_q, a.heads_kv, splits, (int)a.plan.grid);
+  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)(a.batch * a.heads_q)), dim3((unsigned)a.head_dim), 0,
+                     a.stream, ws, static_cast<uint16_t*>(a.o), a.lse, a.heads_q, a.heads_kv, splits, (int)a.plan.grid,
+                     a.head_dim);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_decode_bf16(const AttnArgs& a) {
-  switch (a.head_dim) {
-    case 64: return launch<64>(a);
-    case 128: return launch<128>(a);
-    default: return hipErrorInvalidValue;
-  }
+  if (a.head_dim % 16 != 0 || a.head_dim <= 0 || a.head_dim > 128) return hipErrorInvalidValue;
+  if (a.head_dim == 64) return launch<64, false>(a);
+  if (a.head_dim == 128) return launch<128, false>(a);
+  return a.head_dim < 64 ? launch<64, true>(a) : launch<128, true>(a);
 }
 
 }  // namespace osx

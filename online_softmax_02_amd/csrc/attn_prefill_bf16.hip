@@ -20,7 +20,7 @@
 //    Group B runs one phase behind group A, so on every SIMD one wavefront
 //    feeds the matrix cores while the other runs the exponentials.
 //  * K and V blocks of 64 keys are staged through LDS in 4 stages with 16-byte
-//    direct-to-LDS buffer loads (rows past the end read as 0); stage s holds K
+//    direct-to-LDS buffer loads; stage s holds K
 //    of block j+1 and V of block j for j = s mod 4.  A stage is loaded three
 //    blocks before its MFMA phase, by all 8 wavefronts, and each wavefront
 //    only waits for its loads of the stage two blocks ahead (loads past the
@@ -43,6 +43,16 @@
 //    visited, a wavefront skips the work of blocks that lie wholly after its
 //    own rows, and only blocks that cross the diagonal (or the end of the keys)
 //    are masked; tiles are dispatched heaviest first.
+//  * Every global offset (row, column, block) goes into the buffer
+//    instruction's VGPR offset, which the hardware checks against the
+//    resource's range; the scalar offset, which it does not check, is always
+//    0.  Rows past the end of a head, blocks past the last one and padded
+//    head-dimension columns therefore read as zeros without touching memory.
+//  * A head dimension d that is a multiple of 16 below 64 or between 64 and
+//    128 runs in the 64- or 128-wide kernel: the padded columns of Q, K and V
+//    read as zeros (page "softmax_attention", section 实现思路, pads d up to
+//    the block width and masks the extra lanes the same way), add nothing to
+//    the scores, and are never stored.
 #include <type_traits>
 
 #include "common.hpp"
@@ -55,6 +65,7 @@ constexpr int BN = kBf16BlockN;        // 64 keys per block
 constexpr int kGroupWaves = kPrefillWaves / 2;
 constexpr int kStages = 4;
 constexpr float kRescaleSlack = 8.0f;  // log2 units a row max may exceed the reference before a rescale
+constexpr uint32_t kOffNowhere = 0x80000000u;  // a buffer offset past any head (heads are < 2^31 bytes)
 
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((ext_vector_type(8))) short i16x8;
@@ -104,12 +115,16 @@ __device__ __forceinline__ void phase_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int D>
+// D: the kernel's (padded) head dimension, 64 or 128.  PAD: the true head
+// dimension d_arg (a multiple of 16, at most D) is smaller; global rows are
+// d_arg elements long.
+template <int D, bool PAD>
 __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
     const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, const uint16_t* __restrict__ Vg,
-    uint16_t* __restrict__ Og, float* __restrict__ Lse, int Hq, int Hkv, int Sq, int Sk, int causal, float c, int hp,
-    int n_hgroups, int n_qtiles, int units_per_tile) {
+    uint16_t* __restrict__ Og, float* __restrict__ Lse, int Hq, int Hkv, int Sq, int Sk, int d_arg, int causal,
+    float c, int hp, int n_hgroups, int n_qtiles, int units_per_tile) {
   using T = Bf16Tile<D>;
+  const int d = PAD ? d_arg : D;  // elements per global row
   // One LDS object per stage and operand, so that every access names a fixed object.
   __shared__ __attribute__((aligned(16))) unsigned char lds_k0[T::BLOCK_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char lds_k1[T::BLOCK_BYTES];
@@ -161,7 +176,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
   };
   auto tile_kv_base = [&](int idx) {
     const int rem = idx % units_per_tile;
-    return (size_t)((rem / (Hkv * n_hgroups)) * Hkv + (rem / n_hgroups) % Hkv) * Sk * D;
+    return (size_t)((rem / (Hkv * n_hgroups)) * Hkv + (rem / n_hgroups) % Hkv) * Sk * d;
   };
 
   // The tile whose rows this wavefront is computing: its query head and rows.
@@ -180,7 +195,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
     nblk = tile_nblk(idx);
     wave_live = row0 < Sq;
     wave_row_last = row0 + kRowsPerWave - 1;
-    q_base = (size_t)head * Sq * D;
+    q_base = (size_t)head * Sq * d;
   };
   // Does this wavefront's work include block j of its tile?  (Blocks wholly
   // after its rows do not.)
@@ -188,18 +203,20 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
   // Does block j need the mask for some row of this wavefront?
   auto needs_mask = [&](int j) { return j * BN + BN > Sk || (cmask && j * BN + BN - 1 > row0); };
 
-  // ---- Q as the B operand: lane (query l32, half hf) holds d = 16kc + 8hf .. +8 ----
-  // Rows past Sq read as zeros.
+  // ---- Q as the B operand: lane (query l32, half hf) holds columns 16kc + 8hf .. +8 ----
+  // Rows past Sq and padded columns read as zeros.
   bf16x8 qreg[T::KC];
   auto load_q = [&](int idx) __attribute__((always_inline)) {
     const int qt = tile_qt(idx);
     const int rem = idx % units_per_tile;
     const int hq = (rem / (Hkv * n_hgroups)) * Hq + ((rem / n_hgroups) % Hkv) * G + (rem % n_hgroups) * hp + (wq % hp);
     const int qq = qt * wg_rows + (grp * rs + wq / hp) * kRowsPerWave + l32;
-    const __amdgpu_buffer_rsrc_t qr = make_rsrc(Qg + (size_t)hq * Sq * D, (uint32_t)Sq * D * 2);
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(Qg + (size_t)hq * Sq * d, (uint32_t)Sq * d * 2);
 #pragma unroll
-    for (int kc = 0; kc < T::KC; ++kc)
-      qreg[kc] = __builtin_bit_cast(bf16x8, buf_ld16(qr, (uint32_t)(qq * D + kc * 16 + hf * 8) * 2));
+    for (int kc = 0; kc < T::KC; ++kc) {
+      const int col = kc * 16 + hf * 8;
+      qreg[kc] = __builtin_bit_cast(bf16x8, buf_ld16(qr, col < d ? (uint32_t)(qq * d + col) * 2 : kOffNowhere));
+    }
   };
 
   // ---- global -> LDS staging with buffer_load_dwordx4 ... lds ----
@@ -207,21 +224,33 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
   // fetches the global chunk that belongs in its (swizzled) LDS slot.  One
   // instruction fills LDS_ROWS rows; instructions r * 8 + wave are this
   // wavefront's.  The swizzle of a row depends only on its position within 16
-  // rows, which r does not change: the lane's byte offset is fixed and the
-  // block and instruction offsets go into the scalar soffset.
+  // rows, which r does not change: the lane's byte offset within a block is
+  // fixed (or past the range, for a padded column), and the block and
+  // instruction offsets are added to it.  Everything sits in the range-checked
+  // VGPR offset, so rows past Sk -- the ragged tail and the blocks the load
+  // cursors run through after a workgroup's last block -- read as zeros
+  // without touching memory (a row offset past the range stays past it: a
+  // head is below 2^31 bytes and the cursors run at most a few blocks beyond
+  // it, so no offset wraps).
   const int dma_row = lane / T::CH, dma_chunk = lane % T::CH;
   const int dma_row0 = wave * T::LDS_ROWS + dma_row;
-  const int k_voff = (dma_row0 * D + ((dma_chunk ^ k_swz<T::CH>(dma_row0)) << 3)) * 2;
-  const int v_voff = (dma_row0 * D + ((dma_chunk ^ v_swz<T::CH>(dma_row0)) << 3)) * 2;
-  auto dma_one = [&](const uint16_t* base, int voff, int j0, unsigned char* dst, int r) __attribute__((always_inline)) {
-    // Rows past Sk read as zeros (buffer resource bound).
-    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(base, (uint32_t)Sk * D * 2);
+  const uint32_t k_voff = (dma_chunk ^ k_swz<T::CH>(dma_row0)) * 8 < d
+                              ? (uint32_t)(dma_row0 * d + ((dma_chunk ^ k_swz<T::CH>(dma_row0)) << 3)) * 2
+                              : kOffNowhere;
+  const uint32_t v_voff = (dma_chunk ^ v_swz<T::CH>(dma_row0)) * 8 < d
+                              ? (uint32_t)(dma_row0 * d + ((dma_chunk ^ v_swz<T::CH>(dma_row0)) << 3)) * 2
+                              : kOffNowhere;
+  auto dma_one = [&](const uint16_t* base, uint32_t voff, int j0, unsigned char* dst, int r)
+                     __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(base, (uint32_t)Sk * d * 2);
     const int inst = r * kPrefillWaves + wave;  // uniform
-    // (soffset goes through a local: written inline as the builtin's argument,
-    // this expression kept the host compiler from emitting the launch stub.)
-    const int soff = (j0 + r * kPrefillWaves * T::LDS_ROWS) * D * 2;
+    // A padded column's offset stays past the range as it is (adding the
+    // block offset to it could wrap a 32-bit offset back into the range).
+    const uint32_t off = PAD && voff == kOffNowhere
+                             ? kOffNowhere
+                             : voff + (uint32_t)(j0 + r * kPrefillWaves * T::LDS_ROWS) * (uint32_t)(d * 2);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(dst + inst * 1024), 16,
-                                             voff, soff, 0, 0);
+                                             off, 0, 0, 0);
   };
   // The load stream walks the workgroup's blocks (all its tiles, in order)
   // ahead of the compute: cursor v at the block whose V is loaded next, cursor
@@ -423,7 +452,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
     const float inv = 1.0f / l_tot;
     if (Lse && hf == 0 && q < Sq) Lse[(size_t)head * Sq + q] = (m_ref + log2f(l_tot)) * kLn2;
     if (q < Sq) {
-      uint16_t* op = Og + q_base + (size_t)q * D;
+      uint16_t* op = Og + q_base + (size_t)q * d;
 #pragma unroll
       for (int dt = 0; dt < T::DT; ++dt)
 #pragma unroll
@@ -431,7 +460,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
           const int d0 = 32 * dt + 8 * g + 4 * hf;
           const u32x2 w = {pack_bf16x2(acc[dt][4 * g] * inv, acc[dt][4 * g + 1] * inv),
                            pack_bf16x2(acc[dt][4 * g + 2] * inv, acc[dt][4 * g + 3] * inv)};
-          *reinterpret_cast<u32x2*>(op + d0) = w;
+          if (d0 < d) *reinterpret_cast<u32x2*>(op + d0) = w;  // padded columns are not stored
         }
     }
   };
@@ -539,7 +568,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
   wait_vmcnt<0>();  // no load into LDS may land after the workgroup has ended
 }
 
-template <int D>
+template <int D, bool PAD>
 hipError_t launch(const AttnArgs& a) {
   const int G = a.heads_q / a.heads_kv;
   const int hp = a.plan.heads_per_wg;
@@ -549,26 +578,24 @@ hipError_t launch(const AttnArgs& a) {
   const int units_per_tile = a.batch * a.heads_kv * n_hgroups;
   // One persistent workgroup per CU (fewer when there are fewer tiles); they
   // walk the plan's tiles.
-  int dev = 0, n_cu = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  int n_cu = 0;
+  const hipError_t e = device_cu_count(&n_cu);
   if (e != hipSuccess) return e;
   const int64_t grid = a.plan.grid < n_cu ? a.plan.grid : n_cu;
-  hipLaunchKernelGGL(prefill_bf16_kernel<D>, dim3((unsigned)grid), dim3(kPrefillThreads), 0, a.stream,
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, PAD>), dim3((unsigned)grid), dim3(kPrefillThreads), 0, a.stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse, a.heads_q, a.heads_kv,
-                     a.seq_q, a.seq_k, a.causal, a.c, hp, n_hgroups, n_qtiles, units_per_tile);
+                     a.seq_q, a.seq_k, a.head_dim, a.causal, a.c, hp, n_hgroups, n_qtiles, units_per_tile);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_prefill_bf16(const AttnArgs& a) {
-  switch (a.head_dim) {
-    case 64: return launch<64>(a);
-    case 128: return launch<128>(a);
-    default: return hipErrorInvalidValue;
-  }
+  if (a.head_dim % 16 != 0 || a.head_dim <= 0 || a.head_dim > 128) return hipErrorInvalidValue;
+  if (a.head_dim == 64) return launch<64, false>(a);
+  if (a.head_dim == 128) return launch<128, false>(a);
+  return a.head_dim < 64 ? launch<64, true>(a) : launch<128, true>(a);
 }
 
 }  // namespace osx

@@ -146,15 +146,17 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_f32_kernel(
     const int ch = slot ^ (is_v ? v_swz<T::CH>(row) : k_swz<T::CH>(row));
     return 4 * ch < d ? (uint32_t)(row * d + 4 * ch) * 4 : kOffNowhere;
   };
+  // The block offset is added to the lane's VGPR offset, which the hardware
+  // checks against the range (the scalar offset, which it does not check,
+  // stays 0): rows of the last block past Sk read as zeros without touching
+  // memory, and an offset past the range stays past it.
   auto dma = [&](__amdgpu_buffer_rsrc_t rsrc, bool is_v, unsigned char* dst, int j0) __attribute__((always_inline)) {
 #pragma unroll
     for (int n = 0; n < T::DMA_PER_WAVE; ++n) {
       const int inst = n * kAttnWaves + wave;  // uniform
-      const uint32_t voff = dma_voff(n, is_v);
-      // block offset, uniform (an offset past the range stays past it)
-      const int soff = j0 * d * 4;
+      const uint32_t voff = dma_voff(n, is_v) + (uint32_t)j0 * (uint32_t)(d * 4);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(dst + inst * 1024),
-                                               16, voff, soff, 0, 0);
+                                               16, voff, 0, 0, 0);
     }
   };
   auto load_k = [&](int j0, int buf) { dma(kr, false, lds_k + buf * T::BLOCK_BYTES, j0); };

@@ -80,6 +80,9 @@ constexpr int kProbeThreads = 256;
 constexpr size_t kProbeSinkBytes = (size_t)kProbeWgs * (kProbeThreads / 64) * 4;
 hipError_t launch_read_probe(const void* x, size_t bytes, void* sink, hipStream_t stream);
 
+// Compute units of the current device, queried once per device and cached.
+hipError_t device_cu_count(int* n_cu);
+
 hipError_t launch_prefill_bf16(const AttnArgs& a);
 hipError_t launch_prefill_f32(const AttnArgs& a);
 hipError_t launch_decode_bf16(const AttnArgs& a);

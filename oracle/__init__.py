@@ -22,6 +22,8 @@ recurrence       a blockwise model of the online recurrence (running max, runnin
                  per-key normalised-output recurrence of page "Puzzle 9: Simple
                  FlashAttention" (oracle of the normalised-output variant).
 brute            pure-Python loops over tiny inputs.
+pool             ``attention`` / ``attention_lse`` mapped over (batch, query head)
+                 slices on host threads, for full-size problems.
 
 Every function is pinned by ``tests/test_oracle_pins.py`` to values, closed
 forms and invariants the pages and the mathematics fix.  No function here is
@@ -29,6 +31,8 @@ forms and invariants the pages and the mathematics fix.  No function here is
 """
 from .attention import attention, attention_lse, attention_rows, bf16_bits_to_f64
 from .softmax import softmax_rows
-from . import recurrence, brute
+from . import recurrence, brute, pool
+from .pool import attention_heads
 
-__all__ = ["attention", "attention_lse", "attention_rows", "softmax_rows", "bf16_bits_to_f64", "recurrence", "brute"]
+__all__ = ["attention", "attention_lse", "attention_rows", "attention_heads", "softmax_rows", "bf16_bits_to_f64",
+           "recurrence", "brute", "pool"]

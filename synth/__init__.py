@@ -20,7 +20,7 @@ Recipe (every draw is ``numpy.random.default_rng`` / PCG64):
 from __future__ import annotations
 
 import os
-from concurrent.futures import ProcessPoolExecutor
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -168,9 +168,12 @@ def attn_inputs(w: AttnWorkload, workers: int | None = None) -> dict:
         arr = np.empty(shape, dtype=dt)
         jobs = [(w, name, b, h) for b in range(w.batch) for h in range(heads)]
         if big:
+            # Host threads, not processes: numpy's generators and element-wise
+            # loops release the interpreter lock, and no process is forked
+            # from one that may already hold a GPU context.
             n = workers or min(16, len(os.sched_getaffinity(0)))
-            with ProcessPoolExecutor(max_workers=n) as ex:
-                for (_, _, b, h), s in zip(jobs, ex.map(_fill, jobs, chunksize=8)):
+            with ThreadPoolExecutor(max_workers=n) as ex:
+                for (_, _, b, h), s in zip(jobs, ex.map(_fill, jobs)):
                     arr[b, h] = s
         else:
             for (_, _, b, h) in jobs:

@@ -41,7 +41,9 @@ def test_status_strings():
     ((BF16, 1, 6, 4, 8, 8, 128, 0), osx.OSX_EINVAL),      # heads_q % heads_kv != 0
     ((BF16, 1, 4, 0, 8, 8, 128, 0), osx.OSX_EINVAL),      # no KV heads
     ((F32, 1, 1, 1, 8, 0, 64, 0), osx.OSX_EINVAL),        # empty softmax over keys
-    ((BF16, 1, 1, 1, 8, 8, 96, 0), osx.OSX_EUNSUPPORTED),  # bf16 head_dim
+    ((BF16, 1, 1, 1, 8, 8, 8, 0), osx.OSX_EUNSUPPORTED),   # bf16 head_dim not a multiple of 16
+    ((BF16, 1, 1, 1, 8, 8, 72, 0), osx.OSX_EUNSUPPORTED),  # bf16 head_dim not a multiple of 16
+    ((BF16, 1, 4, 1, 1, 8, 144, 0), osx.OSX_EUNSUPPORTED),  # bf16 head_dim > 128 (decode shape)
     ((F32, 1, 1, 1, 8, 8, 50, 0), osx.OSX_EUNSUPPORTED),   # fp32 head_dim not a multiple of 4
     ((F32, 1, 1, 1, 8, 8, 132, 0), osx.OSX_EUNSUPPORTED),  # fp32 head_dim > 128
     ((BF16, 1, 1, 1, 8, 16, 128, 1), osx.OSX_EUNSUPPORTED),  # causal with Sq != Sk
@@ -253,3 +255,41 @@ def test_non_finite_softmax_scale_is_rejected():
     for bad in (float("nan"), float("inf"), -1.0, 0.0):
         assert lib.osx_softmax_rows_ex(x, y, F32, 2, 16, 0, bad, None, 0, None) == osx.OSX_EINVAL
         assert "scale" in osx.last_error()
+
+
+@pytest.mark.parametrize("d", [16, 32, 48, 64, 80, 96, 112, 128])
+def test_bf16_head_dims_multiple_of_16_are_planned(d):
+    """bf16 accepts every head_dim 16 k <= 128 (page "softmax_attention", section 实现思路, pads d up to the
+    block width); prefill and decode keep the plans of d = 64 / 128 (the padding is inside the kernel)."""
+    p = osx.attn_plan(BF16, 2, 32, 8, 4096, 4096, d, True)
+    ref = osx.attn_plan(BF16, 2, 32, 8, 4096, 4096, 128, True)
+    assert p["kernel_name"] == "prefill_bf16" and p["grid"] == ref["grid"] and p["workspace_bytes"] == 0
+    p = osx.attn_plan(BF16, 4, 16, 4, 1, 1000, d)
+    assert p["kernel_name"] == "decode_bf16" and p["splits"] > 1
+    # the split partials hold d (not the padded width) accumulator columns
+    assert p["workspace_bytes"] == 4 * 4 * p["splits"] * 4 * (2 + d) * 4
+
+
+def test_workspace_bytes_entry_points():
+    """osx_attn_fwd_workspace_bytes / osx_softmax_rows_workspace_bytes return the planned size, 0 when none is
+    needed, and 0 for a rejected problem (the status then comes from the plan call)."""
+    lib = osx.lib
+    for args in [(F32, 1, 1, 1, 4096, 4096, 128, 0), (BF16, 4, 16, 4, 1, 1000, 48, 0),
+                 (BF16, 2, 32, 8, 4096, 4096, 128, 1), (BF16, 64, 32, 8, 1, 8192, 128, 0)]:
+        assert lib.osx_attn_fwd_workspace_bytes(*args) == osx.attn_plan(*args)["workspace_bytes"]
+    assert lib.osx_attn_fwd_workspace_bytes(F32, 1, 1, 1, 4096, 4096, 128, 0) == 4096 * 16 * (2 + 128) * 4
+    assert lib.osx_attn_fwd_workspace_bytes(BF16, 1, 1, 1, 8, 8, 72, 0) == 0
+    assert "multiple of 16" in osx.last_error()
+    assert lib.osx_attn_fwd_workspace_bytes(BF16, 1, 6, 4, 8, 8, 64, 0) == 0
+    for rows, cols in [(1, 1 << 24), (3, 100000), (4, 200), (4096, 2049), (0, 5)]:
+        assert lib.osx_softmax_rows_workspace_bytes(rows, cols) == osx.softmax_rows_workspace(rows, cols)
+    assert lib.osx_softmax_rows_workspace_bytes(1, 1 << 24) == 512 * 8
+    assert lib.osx_softmax_rows_workspace_bytes(2, 0) == 0 and lib.osx_softmax_rows_workspace_bytes(-1, 4) == 0
+
+
+def test_unfused_comparator_keeps_its_head_dims():
+    """The unfused comparator is built for head_dim 64 and 128 only; the fused path takes every 16 k."""
+    with pytest.raises(osx.OsxError) as e:
+        osx.attn_fwd_unfused_workspace(BF16, 1, 4, 1, 128, 128, 96, True)
+    assert e.value.status == osx.OSX_EUNSUPPORTED
+    assert osx.attn_fwd_unfused_workspace(BF16, 1, 4, 1, 128, 128, 64, True) > 0

@@ -69,17 +69,25 @@ def test_lse_of_constant_keys_is_log_count(osx):
     assert err <= 1e-5, err  # P = 1 exactly in bf16: only fp32 rounding of the count remains
 
 
-def test_lse_full_size_prefill_sampled_heads(osx):
-    """The causal GQA prefill workload at full size: LSE of two (batch, head) slices against the oracle."""
-    w = synth.WORKLOADS["gqa_prefill_bf16"]
-    t = synth.attn_inputs(w)
+@pytest.mark.parametrize("case", [("bf16", 2, 16, 4, 1, 5000, 128, False), ("f32", 1, 1, 1, 600, 600, 64, True)],
+                         ids=lambda c: "-".join(map(str, c)))
+def test_binding_allocated_workspace_and_lse(osx, case):
+    """Problems that need a workspace (decode key splits, fp32 key splits), with the workspace and the log-sum-exp
+    both allocated by the binding: the workspace must stay allocated until the launch (it once was freed first, and
+    the log-sum-exp tensor then took its memory), also when the call runs on a side stream."""
+    dtype, B, Hq, Hkv, Sq, Sk, D, causal = case
+    print(f"case binding workspace {case}", flush=True)
+    assert osx.attn_fwd_workspace(osx.OSX_BF16 if dtype == "bf16" else osx.OSX_F32, B, Hq, Hkv, Sq, Sk, D,
+                                  causal) > 0
+    t = synth.random_attn(17, dtype, B, Hq, Hkv, Sq, Sk, D)
     q, k, v = to_dev(t["q"]), to_dev(t["k"]), to_dev(t["v"])
-    _, lse = osx.attn_fwd(q, k, v, causal=True, return_lse=True)
-    torch.cuda.synchronize()
-    got = lse.cpu().numpy()
-    G = w.heads_q // w.heads_kv
-    for b, h in [(0, 5), (1, 30)]:
-        ref = oracle.attention_lse(t["q"][b:b + 1, h:h + 1], t["k"][b:b + 1, h // G:h // G + 1], causal=True)[0, 0]
-        err = float(np.abs(got[b, h] - ref).max())
-        print(f"b{b} h{h}: lse max abs err {err:.3e}")
-        assert err <= LSE_BF16_ATOL
+    ref = oracle.attention(t["q"], t["k"], t["v"], causal=causal)
+    ref_lse = oracle.attention_lse(t["q"], t["k"], causal=causal)
+    bar = LSE_F32_ATOL if dtype == "f32" else LSE_BF16_ATOL
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    for stream in (None, s):
+        out, lse = osx.attn_fwd(q, k, v, causal=causal, return_lse=True, stream=stream)
+        torch.cuda.synchronize()
+        check(to_f64(out), ref, dtype, f"binding workspace {case} stream={stream}")
+        assert float(np.abs(lse.cpu().numpy().astype(np.float64) - ref_lse).max()) <= bar

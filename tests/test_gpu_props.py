@@ -1,8 +1,8 @@
 """Randomised GPU parity sweeps (hypothesis, derandomised so every run draws the same cases).
 
 Small shapes drawn over the whole argument space of each entry point --
-dtypes, GQA group sizes, causal or not, ragged sequence lengths, both head
-dims for bf16, column counts that take each softmax kernel (wavefront,
+dtypes, GQA group sizes, causal or not, ragged sequence lengths, every head
+dim of each dtype, column counts that take each softmax kernel (wavefront,
 workgroup, split), causal periods and scales, the fp32 normalised-output
 variant with and without key splits -- against the fp64 oracle at the
 same bars as the fixed cases.  Outputs start NaN-poisoned, so every element
@@ -38,7 +38,7 @@ def attn_cases(draw):
     batch = draw(st.integers(1, 2))
     hkv = draw(st.integers(1, 2))
     groups = draw(st.sampled_from([1, 2, 3, 4, 8]))
-    d = draw(st.sampled_from([64, 128])) if dtype == "bf16" else 4 * draw(st.integers(1, 32))
+    d = 16 * draw(st.integers(1, 8)) if dtype == "bf16" else 4 * draw(st.integers(1, 32))
     causal = draw(st.booleans())
     sq = draw(st.sampled_from([1, draw(st.integers(2, 160))]))
     sk = sq if (causal and sq > 1) else draw(st.integers(1, 200))

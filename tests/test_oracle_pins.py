@@ -405,3 +405,36 @@ def test_normalised_two_keys_closed_form():
     v = RNG.standard_normal((4, 3))
     o, _, _ = recurrence.attention_normalised(q, k, v, causal=True)
     assert np.array_equal(o[0], v[0])
+
+
+def test_attention_heads_pool_matches_brute_force():
+    """The pooled per-slice driver against pure-Python brute force (GQA groups of 1-3, causal on and off), O and
+    LSE, with several threads: a wrong KV head or a mixed-up slice would miss by O(1)."""
+    for B, Hkv, G, S, D, causal, scale in [(2, 2, 3, 5, 3, True, None), (1, 3, 2, 4, 2, False, 0.7),
+                                           (2, 1, 1, 1, 4, True, 1.3)]:
+        q = RNG.normal(size=(B, Hkv * G, S, D))
+        k = RNG.normal(size=(B, Hkv, S, D))
+        v = RNG.normal(size=(B, Hkv, S, D))
+        o, lse = oracle.attention_heads(q, k, v, causal=causal, scale=scale, with_lse=True, workers=3)
+        ref = np.array(brute.attention(q.tolist(), k.tolist(), v.tolist(), causal=causal, scale=scale))
+        np.testing.assert_allclose(o, ref, rtol=1e-12, atol=1e-13)
+        ref_lse = np.array(brute.attention_lse(q.tolist(), k.tolist(), causal=causal, scale=scale))
+        np.testing.assert_allclose(lse, ref_lse, rtol=1e-12, atol=1e-13)
+
+
+def test_attention_heads_pool_gqa_closed_form_and_subset():
+    """V[b, kv] = 8b + kv gives O[b, h] = 8b + h // G for every head the pool computes; heads left out stay NaN."""
+    B, Hq, Hkv, S, D = 2, 8, 2, 7, 4
+    q, k = RNG.normal(size=(B, Hq, S, D)), RNG.normal(size=(B, Hkv, S, D))
+    v = np.empty((B, Hkv, S, D))
+    for b in range(B):
+        for kv in range(Hkv):
+            v[b, kv] = 8 * b + kv
+    heads = [(0, 0), (0, 3), (0, 4), (1, 7)]
+    o = oracle.attention_heads(q, k, v, causal=True, heads=heads, workers=2)
+    for b in range(B):
+        for h in range(Hq):
+            if (b, h) in heads:
+                np.testing.assert_allclose(o[b, h], 8 * b + h // (Hq // Hkv), rtol=1e-14)
+            else:
+                assert np.isnan(o[b, h]).all()
