@@ -198,6 +198,29 @@ int osx_attn_fwd_unfused(const void* q, const void* k, const void* v, void* o, i
                          int heads_kv, int seq_q, int seq_k, int head_dim, int causal, float scale, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/*
+ * osx_attn_fwd_noalloc -- osx_attn_fwd for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  It takes no workspace and allocates nothing: the partial
+ * (m, l, acc) states that osx_attn_fwd keeps in the caller's workspace go to
+ * a fixed array in the library's own device memory, OSX_NOALLOC_SCRATCH_BYTES
+ * per GPU, held until the process ends.  A problem whose plan needs more
+ * (osx_attn_plan's workspace_bytes) returns OSX_EWORKSPACE before anything is
+ * launched.  No kernel needs the array cleared between calls.
+ *
+ * The first call on each device (with that device current) looks up the
+ * array's device address; make that first call outside any graph capture.
+ * All calls on one GPU share the array: calls that overlap in time on one GPU
+ * (two streams, two host threads) race on it, and the caller must order them.
+ * `stream` must belong to the current device.  lse: NULL, or a device pointer
+ * to batch * heads_q * seq_q fp32 values written as by osx_attn_fwd_lse.
+ * Everything else, errors included, as osx_attn_fwd.
+ */
+#define OSX_NOALLOC_SCRATCH_BYTES (64u << 20)
+int osx_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int dtype, int batch,
+                         int heads_q, int heads_kv, int seq_q, int seq_k, int head_dim, int causal, float scale,
+                         void* stream);
+
 /* osx_softmax_rows_plan -- kernel choice for x[rows, cols]; no HIP calls. */
 int osx_softmax_rows_plan(int64_t rows, int64_t cols, osx_plan* out);
 

@@ -61,6 +61,7 @@ def _load() -> ctypes.CDLL:
     lib.osx_attn_fwd.argtypes = [_vp, _vp, _vp, _vp] + attn_shape + [_f, _vp, _sz, _vp]
     lib.osx_attn_fwd_lse.argtypes = [_vp, _vp, _vp, _vp, _vp] + attn_shape + [_f, _vp, _sz, _vp]
     lib.osx_attn_fwd_normalised.argtypes = [_vp, _vp, _vp, _vp, _vp] + attn_shape + [_f, _vp, _sz, _vp]
+    lib.osx_attn_fwd_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp] + attn_shape + [_f, _vp]
     lib.osx_softmax_rows_plan.argtypes = [_i64, _i64, ctypes.POINTER(Plan)]
     lib.osx_softmax_rows_workspace.argtypes = [_i64, _i64, ctypes.POINTER(_sz)]
     lib.osx_softmax_rows_workspace_bytes.argtypes = [_i64, _i64]
@@ -81,7 +82,7 @@ def _load() -> ctypes.CDLL:
     lib.osx_last_error.restype = ctypes.c_char_p
     lib.osx_version.argtypes = []
     for name in ("osx_attn_plan", "osx_attn_fwd_workspace", "osx_attn_fwd", "osx_attn_fwd_lse",
-                 "osx_attn_fwd_normalised", "osx_softmax_rows_plan",
+                 "osx_attn_fwd_normalised", "osx_attn_fwd_noalloc", "osx_softmax_rows_plan",
                  "osx_softmax_rows_workspace", "osx_softmax_rows", "osx_softmax_rows_ex",
                  "osx_softmax_rows_3pass_workspace", "osx_softmax_rows_3pass", "osx_attn_fwd_unfused_workspace",
                  "osx_attn_fwd_unfused", "osx_version"):
@@ -267,6 +268,33 @@ def attn_fwd_normalised(q, k, v, causal: bool = False, scale: float | None = Non
     return o, (lse.reshape(-1) if squeeze else lse)
 
 
+NOALLOC_SCRATCH_BYTES = 64 << 20  # OSX_NOALLOC_SCRATCH_BYTES
+
+
+def attn_fwd_noalloc(q, k, v, out, causal: bool = False, scale: float | None = None, lse=None, stream=None):
+    """:func:`attn_fwd` through osx_attn_fwd_noalloc: the library's static scratch instead of a workspace.
+
+    ``out`` (and ``lse``, if given) must be supplied: nothing is allocated here.  Calls that overlap in time on one
+    GPU share the scratch and must be ordered by the caller."""
+    squeeze = q.dim() == 2
+    if squeeze:
+        q, k, v, out = q[None, None], k[None, None], v[None, None], out[None, None]
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if t.dim() != 4 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-D (or 2-D) CUDA tensor")
+    if not (q.dtype == k.dtype == v.dtype == out.dtype) or k.shape != v.shape or out.shape != q.shape:
+        raise ValueError("q, k, v, out must share one dtype; k and v one shape; out q's shape")
+    B, Hq, Sq, D = q.shape
+    _, Hkv, Sk, _ = k.shape
+    if lse is not None and (lse.numel() != B * Hq * Sq or not lse.is_contiguous()
+                            or lse.dtype != _torch().float32):
+        raise ValueError("lse must be a contiguous float32 tensor of B * Hq * Sq elements")
+    _check(lib.osx_attn_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                    lse.data_ptr() if lse is not None else None, _dtype_code(q), B, Hq, Hkv, Sq, Sk,
+                                    D, int(causal), float(scale) if scale else 0.0, _stream(q, stream)))
+    return out[0, 0] if squeeze else out
+
+
 def softmax_rows(x, out=None, workspace=None, stream=None, causal_period: int = 0, scale: float = 1.0):
     """y = softmax(scale * x) along the last dimension of a contiguous float32 or bfloat16 CUDA tensor.
 
@@ -379,4 +407,4 @@ __all__ = ["attn_fwd", "softmax_rows", "attn_plan", "attn_fwd_workspace", "softm
            "softmax_rows_workspace", "status_string", "last_error", "version", "OsxError", "lib", "LIB_PATH",
            "OSX_F32", "OSX_BF16", "softmax_rows_3pass", "softmax_rows_3pass_workspace", "OSX_3PASS_ATOMIC",
            "OSX_3PASS_STASH", "attn_fwd_unfused", "attn_fwd_unfused_workspace", "attn_fwd_normalised",
-           "read_probe"]
+           "read_probe", "attn_fwd_noalloc", "NOALLOC_SCRATCH_BYTES"]

@@ -27,6 +27,7 @@ SOURCES = [
     "attn_decode_bf16.hip",
     "attn_unfused.hip",
     "read_probe.hip",
+    "noalloc.hip",
 ]
 
 ARCH = "gfx950"

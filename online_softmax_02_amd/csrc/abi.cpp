@@ -307,6 +307,25 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, b
 
 }  // namespace
 
+namespace osx {
+
+int attn_fwd_call(const void* q, const void* k, const void* v, void* o, float* lse, bool want_lse, int dtype,
+                  int batch, int heads_q, int heads_kv, int seq_q, int seq_k, int head_dim, int causal, float scale,
+                  void* workspace, size_t workspace_bytes, void* stream, bool normalised) {
+  return attn_fwd(q, k, v, o, lse, want_lse, dtype, batch, heads_q, heads_kv, seq_q, seq_k, head_dim, causal, scale,
+                  workspace, workspace_bytes, stream, normalised);
+}
+
+int set_error(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+}  // namespace osx
+
 extern "C" {
 
 int osx_attn_fwd(const void* q, const void* k, const void* v, void* o, int dtype, int batch, int heads_q,

@@ -83,6 +83,15 @@ hipError_t launch_read_probe(const void* x, size_t bytes, void* sink, hipStream_
 // Compute units of the current device, queried once per device and cached.
 hipError_t device_cu_count(int* n_cu);
 
+// The checked attention call behind osx_attn_fwd / _lse / _normalised
+// (argument checks, plan, launch); returns an OSX_* status and sets the
+// thread's error message.
+int attn_fwd_call(const void* q, const void* k, const void* v, void* o, float* lse, bool want_lse, int dtype,
+                  int batch, int heads_q, int heads_kv, int seq_q, int seq_k, int head_dim, int causal, float scale,
+                  void* workspace, size_t workspace_bytes, void* stream, bool normalised);
+// Sets the thread's error message (printf format) and returns `status`.
+int set_error(int status, const char* fmt, ...);
+
 hipError_t launch_prefill_bf16(const AttnArgs& a);
 hipError_t launch_prefill_f32(const AttnArgs& a);
 hipError_t launch_decode_bf16(const AttnArgs& a);
