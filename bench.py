@@ -17,9 +17,16 @@ as the reference for the HBM-bound lines, a plain 16-byte streaming read of
 2 GiB on the same GPU.
 
 Inputs are seeded synthetic tensors (``synth``), generated on the host and
-copied to HBM before timing.  Durations come from one HIP event pair recorded
-on the stream the kernels run on, around the whole timed region of
-back-to-back calls, divided by the number of calls.
+copied to HBM before timing.  Durations come from HIP events recorded on the
+stream the kernels run on: the timed calls run back to back in a few
+consecutive windows, each bracketed by its own event pair, so the mean over
+all calls (the reported rate) and the per-call min / median / max over the
+windows come from the same run.
+
+``cpu_baseline`` times the fp64 oracle on the host's cores in the same run:
+every workload in full (the per-(batch, head) slices of the large ones spread
+over a pool of host threads), each with its wall time and its rate under the
+same algorithmic count as the GPU line.
 
 ``--gpus N`` with N > 1 exits: the library and this benchmark use one GPU.
 Prints one JSON line on stdout.
@@ -57,7 +64,6 @@ def parse():
                    choices=["all", "prefill", "unfused", "decode", "softmax", "f32", "small", "copy", "probe"],
                    help="time one workload only (for profiler runs)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle timing sample")
     return p.parse_args()
 
 
@@ -82,15 +88,37 @@ def traffic_for(kernel: str):
     return rec.get("traffic_bytes_per_launch")
 
 
+WINDOWS = 5  # event windows per timed region
+
+
+class Timing:
+    """Result of timed(): wall seconds of the timed region, mean GPU ms per call over all calls, and the mean ms
+    per call of each event window."""
+
+    def __init__(self, wall, ms, window_ms):
+        self.wall, self.ms, self.window_ms = wall, ms, window_ms
+
+    def __iter__(self):  # (wall, ms) unpacking
+        return iter((self.wall, self.ms))
+
+    def per_call_us(self):
+        w = sorted(self.window_ms)
+        med = w[len(w) // 2] if len(w) % 2 else 0.5 * (w[len(w) // 2 - 1] + w[len(w) // 2])
+        return {"mean": round(self.ms * 1e3, 2), "min": round(w[0] * 1e3, 2), "median": round(med * 1e3, 2),
+                "max": round(w[-1] * 1e3, 2), "windows": len(w)}
+
+
 def timed(torch, fn, steps, warmup):
     """Warm up, then time `steps` back-to-back calls.
 
     The call first runs untimed for PREWARM_S seconds (GPU clocks ramp up
-    over the first few hundred milliseconds), then `warmup` times.
-    One HIP event pair on the launch stream brackets the whole timed region, so
-    the host keeps the GPU queue full (per-call event pairs would count the
-    host's argument marshalling whenever the GPU catches up).  Returns
-    (wall seconds, mean GPU ms per call)."""
+    over the first few hundred milliseconds), then `warmup` times.  The timed
+    calls are split into up to WINDOWS consecutive windows, each bracketed by
+    a HIP event pair on the launch stream; the windows follow each other with
+    no host synchronisation, so the host keeps the GPU queue full (per-call
+    event pairs would count the host's argument marshalling whenever the GPU
+    catches up).  Returns a Timing: the mean over all `steps` calls is the
+    first window's start to the last window's end."""
     # Bring the GPU clocks up first: run the call for ~0.5 s (untimed).
     t_end = time.perf_counter() + PREWARM_S
     while time.perf_counter() < t_end:
@@ -100,16 +128,22 @@ def timed(torch, fn, steps, warmup):
     for i in range(warmup):
         fn(i)
     stream = torch.cuda.current_stream()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n_win = max(1, min(WINDOWS, steps))
+    sizes = [steps // n_win + (1 if w < steps % n_win else 0) for w in range(n_win)]
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(n_win + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    start.record(stream)
-    for i in range(steps):
-        fn(warmup + i)
-    end.record(stream)
+    events[0].record(stream)
+    i = 0
+    for w, n in enumerate(sizes):
+        for _ in range(n):
+            fn(warmup + i)
+            i += 1
+        events[w + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall, start.elapsed_time(end) / steps
+    window_ms = [events[w].elapsed_time(events[w + 1]) / n for w, n in enumerate(sizes)]
+    return Timing(wall, events[0].elapsed_time(events[-1]) / steps, window_ms)
 
 
 def to_dev(a):
@@ -139,9 +173,11 @@ def bench_prefill(torch, osx, args):
     w = synth.WORKLOADS["gqa_prefill_bf16"]
     t, q, k, v = attn_tensors(torch, w)
     out = torch.empty_like(q)
-    wall, kern_ms = timed(torch, lambda i: osx.attn_fwd(q, k, v, causal=True, out=out), args.steps, args.warmup)
+    tm = timed(torch, lambda i: osx.attn_fwd(q, k, v, causal=True, out=out), args.steps, args.warmup)
+    wall, kern_ms = tm
     tflops = w.flops() / (kern_ms * 1e-3) / 1e12
     res = {"wall_s": wall, "ms_per_step": wall / args.steps * 1e3, "kernel_ms": kern_ms, "tflops": tflops,
+           "per_call_us": tm.per_call_us(),
            "roofline": roofline("mfma", tflops, PEAK_BF16_TFLOPS, "TFLOP/s", traffic_for("prefill_bf16_kernel")),
            "qkv": (q, k, v)}
     return res, t, w
@@ -155,13 +191,14 @@ def bench_unfused(torch, osx, args, q, k, v, w, fused_ms):
     ws = torch.empty(osx.attn_fwd_unfused_workspace(osx.OSX_BF16, w.batch, w.heads_q, w.heads_kv, w.seq_q, w.seq_k,
                                                     w.head_dim, True), dtype=torch.uint8, device="cuda")
     steps = max(3, args.steps // 4)
-    _, ms = timed(torch, lambda i: osx.attn_fwd_unfused(q, k, v, causal=True, out=out, workspace=ws), steps,
-                  args.warmup)
+    tm = timed(torch, lambda i: osx.attn_fwd_unfused(q, k, v, causal=True, out=out, workspace=ws), steps,
+               args.warmup)
+    ms = tm.ms
     scores = float(w.batch * w.heads_q * w.seq_q * w.seq_k)
     nbytes = 16.0 * scores + w.bytes()
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"workload": w.name, "unit": "GB/s", "value": round(gbs, 1), "call_us": round(ms * 1e3, 2),
-            "bytes_per_call": nbytes, "score_matrix_bytes": 4.0 * scores,
+            "per_call_us": tm.per_call_us(), "bytes_per_call": nbytes, "score_matrix_bytes": 4.0 * scores,
             "tflops_causal_adjusted": round(w.flops() / (ms * 1e-3) / 1e12, 2),
             "time_vs_fused": round(ms / fused_ms, 2),
             "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", None)}
@@ -170,15 +207,16 @@ def bench_unfused(torch, osx, args, q, k, v, w, fused_ms):
 def bench_decode(torch, osx, args):
     import synth
     w = synth.WORKLOADS["gqa_decode_bf16"]
-    _, q, k, v = attn_tensors(torch, w)
+    t, q, k, v = attn_tensors(torch, w)
     out = torch.empty_like(q)
     ws = torch.empty(osx.attn_fwd_workspace(osx.OSX_BF16, w.batch, w.heads_q, w.heads_kv, 1, w.seq_k, w.head_dim),
                      dtype=torch.uint8, device="cuda")
-    wall, ms = timed(torch, lambda i: osx.attn_fwd(q, k, v, out=out, workspace=ws), args.steps, args.warmup)
+    tm = timed(torch, lambda i: osx.attn_fwd(q, k, v, out=out, workspace=ws), args.steps, args.warmup)
+    ms = tm.ms
     gbs = w.bytes() / (ms * 1e-3) / 1e9
     return {"workload": w.name, "unit": "GB/s", "value": round(gbs, 1), "call_us": round(ms * 1e3, 2),
-            "bytes_per_call": w.bytes(),
-            "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", traffic_for("decode_bf16_kernel"))}
+            "per_call_us": tm.per_call_us(), "bytes_per_call": w.bytes(),
+            "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", traffic_for("decode_bf16_kernel"))}, t
 
 
 def softmax_reads(osx, w):
@@ -194,12 +232,12 @@ def bench_softmax(torch, osx, args):
     xs = [x.clone() for _ in range(5)]
     ys = [torch.empty_like(x) for _ in range(5)]
     ws = torch.empty(osx.softmax_rows_workspace(w.rows, w.cols), dtype=torch.uint8, device="cuda")
-    wall, ms = timed(torch, lambda i: osx.softmax_rows(xs[i % 5], out=ys[i % 5], workspace=ws), args.steps,
-                     args.warmup)
+    tm = timed(torch, lambda i: osx.softmax_rows(xs[i % 5], out=ys[i % 5], workspace=ws), args.steps, args.warmup)
+    ms = tm.ms
     reads = softmax_reads(osx, w)
     gbs = w.bytes(reads) / (ms * 1e-3) / 1e9
     return {"workload": w.name, "unit": "GB/s", "value": round(gbs, 1), "call_us": round(ms * 1e3, 2),
-            "bytes_per_call": w.bytes(reads), "reads_of_x": reads,
+            "per_call_us": tm.per_call_us(), "bytes_per_call": w.bytes(reads), "reads_of_x": reads,
             "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", traffic_for("softmax_split"))}
 
 
@@ -216,13 +254,15 @@ def bench_softmax_3pass(torch, osx, args, two_pass_us):
     out = {}
     for name, method, passes in (("atomic", osx.OSX_3PASS_ATOMIC, 4), ("stash", osx.OSX_3PASS_STASH, 5)):
         ws = torch.empty(osx.softmax_rows_3pass_workspace(w.rows, w.cols, method), dtype=torch.uint8, device="cuda")
-        _, ms = timed(torch, lambda i: osx.softmax_rows_3pass(xs[i % 5], method, out=ys[i % 5], workspace=ws),
-                      args.steps, args.warmup)
+        tm = timed(torch, lambda i: osx.softmax_rows_3pass(xs[i % 5], method, out=ys[i % 5], workspace=ws),
+                   args.steps, args.warmup)
+        ms = tm.ms
         nbytes = passes * 4.0 * w.rows * w.cols
         gbs = nbytes / (ms * 1e-3) / 1e9
         out[f"softmax_1x16m_3pass_{name}"] = {
             "workload": w.name, "unit": "GB/s", "value": round(gbs, 1), "call_us": round(ms * 1e3, 2),
-            "bytes_per_call": nbytes, "time_vs_two_pass": round(ms * 1e3 / two_pass_us, 3),
+            "per_call_us": tm.per_call_us(), "bytes_per_call": nbytes,
+            "time_vs_two_pass": round(ms * 1e3 / two_pass_us, 3),
             "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", None)}
     return out
 
@@ -236,25 +276,28 @@ def bench_softmax_causal(torch, osx, args):
     xs = [x.clone() for _ in range(5)]
     ys = [torch.empty_like(x) for _ in range(5)]
     ws = torch.empty(max(1, osx.softmax_rows_workspace(w.rows, w.cols)), dtype=torch.uint8, device="cuda")
-    wall, ms = timed(torch, lambda i: osx.softmax_rows(xs[i % 5], out=ys[i % 5], workspace=ws,
-                                                       causal_period=w.causal_period, scale=w.scale),
-                     args.steps, args.warmup)
+    tm = timed(torch, lambda i: osx.softmax_rows(xs[i % 5], out=ys[i % 5], workspace=ws,
+                                                 causal_period=w.causal_period, scale=w.scale),
+               args.steps, args.warmup)
+    ms = tm.ms
     reads = softmax_reads(osx, w)
     gbs = w.bytes(reads) / (ms * 1e-3) / 1e9
     return {"workload": w.name, "unit": "GB/s", "value": round(gbs, 1), "call_us": round(ms * 1e3, 2),
-            "bytes_per_call": w.bytes(reads), "reads_of_x": reads,
+            "per_call_us": tm.per_call_us(), "bytes_per_call": w.bytes(reads), "reads_of_x": reads,
             "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", traffic_for("softmax_wave_causal"))}
 
 
 def bench_f32(torch, osx, args):
     import synth
     w = synth.WORKLOADS["attn_f32_4k_d128"]
-    _, q, k, v = attn_tensors(torch, w)
+    t, q, k, v = attn_tensors(torch, w)
     out = torch.empty_like(q)
-    wall, ms = timed(torch, lambda i: osx.attn_fwd(q, k, v, out=out), args.steps, args.warmup)
+    tm = timed(torch, lambda i: osx.attn_fwd(q, k, v, out=out), args.steps, args.warmup)
+    ms = tm.ms
     tf = w.flops() / (ms * 1e-3) / 1e12
     return {"workload": w.name, "unit": "TFLOP/s", "value": round(tf, 2), "call_us": round(ms * 1e3, 2),
-            "roofline": roofline("mfma", tf, PEAK_F32_TFLOPS, "TFLOP/s", traffic_for("prefill_f32_kernel"))}
+            "per_call_us": tm.per_call_us(),
+            "roofline": roofline("mfma", tf, PEAK_F32_TFLOPS, "TFLOP/s", traffic_for("prefill_f32_kernel"))}, t
 
 
 def bench_f32_normalised(torch, osx, args, plain_us):
@@ -263,9 +306,11 @@ def bench_f32_normalised(torch, osx, args, plain_us):
     w = synth.WORKLOADS["attn_f32_4k_d128"]
     _, q, k, v = attn_tensors(torch, w)
     out = torch.empty_like(q)
-    wall, ms = timed(torch, lambda i: osx.attn_fwd_normalised(q, k, v, out=out), args.steps, args.warmup)
+    tm = timed(torch, lambda i: osx.attn_fwd_normalised(q, k, v, out=out), args.steps, args.warmup)
+    ms = tm.ms
     tf = w.flops() / (ms * 1e-3) / 1e12
     return {"workload": w.name, "unit": "TFLOP/s", "value": round(tf, 2), "call_us": round(ms * 1e3, 2),
+            "per_call_us": tm.per_call_us(),
             "time_vs_unnormalised": round(ms * 1e3 / plain_us, 3),
             "roofline": roofline("mfma", tf, PEAK_F32_TFLOPS, "TFLOP/s", None)}
 
@@ -274,9 +319,11 @@ def bench_lse(torch, osx, args, q, k, v, w, plain_ms):
     """The prefill call that also writes each query row's log-sum-exp (osx_attn_fwd_lse)."""
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-    wall, ms = timed(torch, lambda i: osx.attn_fwd(q, k, v, causal=True, out=out, lse=lse), args.steps, args.warmup)
+    tm = timed(torch, lambda i: osx.attn_fwd(q, k, v, causal=True, out=out, lse=lse), args.steps, args.warmup)
+    ms = tm.ms
     tf = w.flops() / (ms * 1e-3) / 1e12
     return {"workload": w.name, "unit": "TFLOP/s", "value": round(tf, 2), "call_us": round(ms * 1e3, 2),
+            "per_call_us": tm.per_call_us(),
             "time_vs_without_lse": round(ms / plain_ms, 3),
             "roofline": roofline("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s", None)}
 
@@ -287,14 +334,14 @@ def bench_small(torch, osx, args):
     w = synth.WORKLOADS["attn_f32_m64_n100_d48"]
     _, q, k, v = attn_tensors(torch, w)
     out = torch.empty_like(q)
-    _, ms = timed(torch, lambda i: osx.attn_fwd(q, k, v, out=out), args.steps, args.warmup)
-    res[w.name] = {"unit": "us", "value": round(1e3 * ms, 2),
+    tm = timed(torch, lambda i: osx.attn_fwd(q, k, v, out=out), args.steps, args.warmup)
+    res[w.name] = {"unit": "us", "value": round(1e3 * tm.ms, 2), "per_call_us": tm.per_call_us(),
                    "note": "launch-latency bound; roofline fraction not meaningful"}
     w = synth.WORKLOADS["softmax_4x200"]
     x = to_dev(synth.softmax_inputs(w))
     y = torch.empty_like(x)
-    _, ms = timed(torch, lambda i: osx.softmax_rows(x, out=y), args.steps, args.warmup)
-    res[w.name] = {"unit": "us", "value": round(1e3 * ms, 2),
+    tm = timed(torch, lambda i: osx.softmax_rows(x, out=y), args.steps, args.warmup)
+    res[w.name] = {"unit": "us", "value": round(1e3 * tm.ms, 2), "per_call_us": tm.per_call_us(),
                    "note": "launch-latency bound; roofline fraction not meaningful"}
     return res
 
@@ -304,9 +351,11 @@ def bench_read_probe(torch, osx, args):
     n = 1 << 29
     x = torch.ones(n, dtype=torch.int32, device="cuda")
     sink = torch.empty(osx.lib.osx_read_probe_sink_bytes() // 4, dtype=torch.int32, device="cuda")
-    _, ms = timed(torch, lambda i: osx.read_probe(x, sink=sink), args.steps, args.warmup)
+    tm = timed(torch, lambda i: osx.read_probe(x, sink=sink), args.steps, args.warmup)
+    ms = tm.ms
     gbs = 4.0 * n / (ms * 1e-3) / 1e9
     return {"workload": "read 2 GiB", "unit": "GB/s", "value": round(gbs, 1), "call_us": round(ms * 1e3, 2),
+            "per_call_us": tm.per_call_us(),
             "note": "achievable-bandwidth reference (loads only), not a step of the method",
             "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", None)}
 
@@ -320,28 +369,59 @@ def bench_copy(torch, args):
     return {"bytes_read": 4 * n, "bytes_written": 4 * n}
 
 
-def cpu_baseline(t, w, seconds):
-    """The fp64 oracle on whole (batch, head) slices of the prefill workload, timed on the host."""
-    import numpy as np
+def cpu_baseline(host):
+    """The fp64 oracle, timed on the host's cores, on every workload in full.
+
+    ``host`` maps workload names to the host inputs the GPU lines used (the
+    rest are regenerated from their seeds).  Single-head workloads call the
+    oracle once (numpy's BLAS uses every core for the products; the
+    element-wise steps run on one thread); the multi-head ones spread their
+    (batch, query head) slices over ``oracle.attention_heads``' pool of host
+    threads.  Each entry gives the wall time and the rate under the GPU line's
+    algorithmic count; the causal prefill's rate uses the causal-adjusted flop
+    count although the oracle computes the dense score matrix.  The headline
+    value is the causal GQA prefill's."""
     import oracle
+    import synth
     cores = len(os.sched_getaffinity(0))
-    G = w.groups
-    heads = [(b, h) for b in range(w.batch) for h in range(w.heads_q)]
-    order = np.random.default_rng(0).permutation(len(heads))
-    rows = np.arange(w.seq_q)
-    done = 0
-    t0 = time.perf_counter()
-    for idx in order:
-        b, h = heads[idx]
-        oracle.attention_rows(t["q"][b, h], t["k"][b, h // G], t["v"][b, h // G], rows, causal=True, seq_q=w.seq_q)
-        done += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    el = time.perf_counter() - t0
-    flops = done * 4.0 * w.seq_q * w.seq_k * w.head_dim * 0.5
-    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{done} of {len(heads)} (batch, query head) slices of {w.name}, all {w.seq_q} rows each, "
-                      f"{el:.1f}s; causal-adjusted flop count (the oracle computes the dense score matrix)"}
+    workers = oracle.pool.default_workers()
+    per = {}
+
+    def run(name, fn, work, unit, threads, what):
+        t0 = time.perf_counter()
+        fn()
+        el = time.perf_counter() - t0
+        scale = 1e12 if unit == "TFLOP/s" else 1e9
+        per[name] = {"wall_s": round(el, 6), "value": round(work / el / scale, 6), "unit": unit,
+                     "threads": threads, "what": what}
+        log(f"[bench] oracle {name}: {el:.2f}s")
+
+    W = synth.WORKLOADS
+    w = W["attn_f32_m64_n100_d48"]
+    t = synth.attn_inputs(w)
+    run(w.name, lambda: oracle.attention(t["q"], t["k"], t["v"]), w.flops(), "TFLOP/s", cores, "oracle.attention")
+    for name in ("softmax_4x200", "softmax_1x16m"):
+        w = W[name]
+        x = synth.softmax_inputs(w)
+        run(name, lambda: oracle.softmax_rows(x), w.bytes(2 if w.cols > 8192 else 1), "GB/s", 1,
+            "oracle.softmax_rows")
+    w = W["attn_f32_4k_d128"]
+    t = host.get(w.name) or synth.attn_inputs(w)
+    run(w.name, lambda: oracle.attention(t["q"], t["k"], t["v"]), w.flops(), "TFLOP/s", cores, "oracle.attention")
+    w = W["gqa_decode_bf16"]
+    t = host.get(w.name) or synth.attn_inputs(w)
+    run(w.name, lambda: oracle.attention_heads(t["q"], t["k"], t["v"], workers=workers), w.bytes(), "GB/s", workers,
+        f"oracle.attention_heads, {w.batch * w.heads_q} heads on {workers} threads")
+    w = W["gqa_prefill_bf16"]
+    t = host[w.name]
+    run(w.name, lambda: oracle.attention_heads(t["q"], t["k"], t["v"], causal=True, workers=workers), w.flops(),
+        "TFLOP/s", workers, f"oracle.attention_heads, {w.batch * w.heads_q} heads on {workers} threads")
+    head = per[w.name]
+    return {"value": head["value"], "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+            "sample": f"all {w.batch * w.heads_q} (batch, query head) slices of {w.name} (the whole workload), "
+                      f"{head['wall_s']}s on a pool of {workers} host threads (BLAS one thread per call); "
+                      "causal-adjusted flop count (the oracle computes the dense score matrix)",
+            "per_config": per}
 
 
 def main():
@@ -364,7 +444,7 @@ def main():
         print(json.dumps({"also": {"hbm_read_probe": bench_read_probe(torch, osx, args)}}))
         return
     if args.only in ("decode",):
-        also["gqa_decode_bf16"] = bench_decode(torch, osx, args)
+        also["gqa_decode_bf16"], _ = bench_decode(torch, osx, args)
         print(json.dumps({"also": also}))
         return
     if args.only in ("softmax",):
@@ -374,7 +454,7 @@ def main():
         print(json.dumps({"also": also}))
         return
     if args.only in ("f32",):
-        also["attn_f32_4k_d128"] = bench_f32(torch, osx, args)
+        also["attn_f32_4k_d128"], _ = bench_f32(torch, osx, args)
         also["attn_f32_normalised_4k_d128"] = bench_f32_normalised(torch, osx, args,
                                                                    also["attn_f32_4k_d128"]["call_us"])
         print(json.dumps({"also": also}))
@@ -384,6 +464,7 @@ def main():
         return
 
     head, t, w = bench_prefill(torch, osx, args)
+    host = {w.name: t}
     log(f"[bench] prefill {head['tflops']:.1f} TFLOP/s ({head['kernel_ms']:.3f} ms per call)")
     qkv = head.pop("qkv")
     if args.only in ("all", "unfused"):
@@ -399,7 +480,7 @@ def main():
     if args.only == "all":
         also["hbm_read_probe"] = bench_read_probe(torch, osx, args)
         log(f"[bench] plain streaming read {also['hbm_read_probe']['value']} GB/s")
-        also["gqa_decode_bf16"] = bench_decode(torch, osx, args)
+        also["gqa_decode_bf16"], host["gqa_decode_bf16"] = bench_decode(torch, osx, args)
         log(f"[bench] decode {also['gqa_decode_bf16']['value']} GB/s")
         also["softmax_1x16m"] = bench_softmax(torch, osx, args)
         log(f"[bench] softmax {also['softmax_1x16m']['value']} GB/s")
@@ -407,7 +488,7 @@ def main():
         log(f"[bench] causal bf16 softmax {also['softmax_causal_bf16']['value']} GB/s")
         also.update(bench_softmax_3pass(torch, osx, args, also["softmax_1x16m"]["call_us"]))
         log("[bench] three-pass comparators done")
-        also["attn_f32_4k_d128"] = bench_f32(torch, osx, args)
+        also["attn_f32_4k_d128"], host["attn_f32_4k_d128"] = bench_f32(torch, osx, args)
         log(f"[bench] fp32 attention {also['attn_f32_4k_d128']['value']} TFLOP/s")
         also["attn_f32_normalised_4k_d128"] = bench_f32_normalised(torch, osx, args,
                                                                    also["attn_f32_4k_d128"]["call_us"])
@@ -416,7 +497,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline and args.only == "all":
         log("[bench] timing the oracle on the host")
-        cpu = cpu_baseline(t, w, args.cpu_seconds)
+        cpu = cpu_baseline(host)
     rec = {
         "metric": METRIC,
         "value": round(head["tflops"], 2),
@@ -434,6 +515,7 @@ def main():
                    "seq_q": w.seq_q, "seq_k": w.seq_k, "head_dim": w.head_dim, "causal": w.causal,
                    "parallelism": "none (one GPU)"},
         "kernel_ms": round(head["kernel_ms"], 4),
+        "per_call_us": head["per_call_us"],
         "roofline": head["roofline"],
         "cpu_baseline": cpu,
         "also": also,

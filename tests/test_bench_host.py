@@ -38,3 +38,33 @@ def test_softmax_read_count_follows_the_plan():
     assert bench.softmax_reads(osx, synth.WORKLOADS["softmax_1x16m"]) == 2
     assert bench.softmax_reads(osx, synth.WORKLOADS["softmax_causal_bf16"]) == 1
     assert bench.softmax_reads(osx, synth.WORKLOADS["softmax_4x200"]) == 1
+
+
+def test_timing_statistics():
+    """Per-call min / median / max come from the event windows; the mean is over all calls."""
+    tm = bench.Timing(1.0, 0.25, [0.3, 0.2, 0.25, 0.22, 0.28])
+    assert tm.per_call_us() == {"mean": 250.0, "min": 200.0, "median": 250.0, "max": 300.0, "windows": 5}
+    assert bench.Timing(1.0, 0.5, [0.4, 0.6]).per_call_us()["median"] == 500.0
+    wall, ms = tm
+    assert (wall, ms) == (1.0, 0.25)
+
+
+ALGORITHMIC = {  # the byte counts the bench lines divide by, from the workload definitions
+    "prefill_bf16_kernel": synth.WORKLOADS["gqa_prefill_bf16"].bytes(),
+    "decode_bf16_kernel": synth.WORKLOADS["gqa_decode_bf16"].bytes(),
+    "softmax_split": synth.WORKLOADS["softmax_1x16m"].bytes(2),
+    "softmax_wave_causal": synth.WORKLOADS["softmax_causal_bf16"].bytes(1),
+    "prefill_f32_kernel": synth.WORKLOADS["attn_f32_4k_d128"].bytes(),
+}
+
+
+@pytest.mark.parametrize("kernel", sorted(ALGORITHMIC))
+def test_profile_records_use_the_workload_byte_counts(kernel):
+    """Every committed counter record states the algorithmic bytes of its workload (Q, K, V read once and O written
+    once for attention; x read as often as the plan needs and y written once for the softmax)."""
+    path = os.path.join(bench.ROOT, "profiles", f"pmc_{kernel}.json")
+    if not os.path.exists(path):
+        pytest.skip("no counter record")
+    with open(path) as f:
+        rec = json.load(f)
+    assert rec["algorithmic_bytes_per_launch"] == int(ALGORITHMIC[kernel])
