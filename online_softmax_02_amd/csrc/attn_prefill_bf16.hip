@@ -22,11 +22,13 @@
 //  * K and V blocks of 64 keys are staged through LDS in 4 stages with 16-byte
 //    direct-to-LDS buffer loads; stage s holds K
 //    of block j+1 and V of block j for j = s mod 4.  A stage is loaded three
-//    blocks before its MFMA phase, by all 8 wavefronts, and each wavefront
-//    only waits for its loads of the stage two blocks ahead (loads past the
-//    last block are issued anyway, so every wait has a fixed count).  The loop is
-//    unrolled by 4 so every stage is a fixed LDS object: the compiler then
+//    blocks before its MFMA phase, by all 8 wavefronts, each of which waits
+//    for all its loads at the end of its next softmax phase (loads past the
+//    last block are issued anyway, so every wait has a fixed count).  The loop
+//    is unrolled by 4 so every stage is a fixed LDS object: the compiler then
 //    knows that a read of one stage does not wait for a load into another.
+//  * Row sums l of the bf16 weights are taken on the matrix cores too, with a
+//    16x16x32 MFMA per 16 keys that reads the PV step's P^T register as is.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //    a lane then holds 16 scores of ONE query, so the row max and row sum are
 //    lane-local (plus one permlane exchange between the two lane halves) and
@@ -320,10 +322,18 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
 #pragma unroll
   for (int i = 0; i < T::DT; ++i) acc[i] = f32x16{};
   float m_ref = kNegInf;
-  // Row sums of the bf16 weights, accumulated on the matrix cores: an A
-  // operand of ones turns each PV step into a row sum, so every element of
-  // this tile holds l for the lane's query (in fp32, exactly as the PV sees P).
-  f32x16 acc_l = f32x16{};
+  // Row sums of the bf16 weights, accumulated on the matrix cores (in fp32,
+  // exactly as the PV sees P) with a 16x16x32 MFMA: its B operand is the P^T
+  // register of the PV step as it is, which it reads as 16 columns n of four
+  // 8-key groups (queries n and n + 16, both lane halves); an A operand that
+  // selects groups 0 and 2 for output rows 0-7 and groups 1 and 3 for rows
+  // 8-15 makes rows 0-7 the sums of query n and rows 8-15 those of query
+  // n + 16.  Half the matrix cycles of a 32x32x16 MFMA with an all-ones A and
+  // a quarter of its registers; lanes 16-31 then hold the sum of query
+  // l32 - 16 and lanes 32-47 that of query l32 + 16 (rows 1 and 2 of the
+  // wavefront swapped), which the rare rescale and the epilogue undo.
+  f32x4 acc_l = f32x4{};
+  const int l_src = (lane >> 4) == 1 ? lane + 16 : ((lane >> 4) == 2 ? lane - 16 : lane);
   f32x16 s[2];      // scores of the block the next softmax phase handles
   bf16x8 pb[2][2];  // its bf16 weights, the B operand of the next PV
 
@@ -361,7 +371,8 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
     constexpr int kDmaEvery = NQ / (2 * T::DMA_PER_WAVE);
-    const bf16x8 kOnes = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+    const uint32_t sel = ((lane >> 4) & 1) == ((lane & 15) >> 3) ? 0x3f803f80u : 0u;  // bf16 1.0 pairs or 0
+    const bf16x8 kSel = __builtin_bit_cast(bf16x8, u32x4{sel, sel, sel, sel});
     bf16x8 ring[kRing];
 #pragma unroll
     for (int m = 0; m < kAhead; ++m) ring[m % kRing] = frag(m);
@@ -370,7 +381,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
 #pragma unroll
     for (int tu = 0; tu < 4; ++tu) {
       __builtin_amdgcn_sched_barrier(0);
-      acc_l = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kOnes, pb[tu >> 1][tu & 1], acc_l, 0, 0, 0);
+      acc_l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kSel, pb[tu >> 1][tu & 1], acc_l, 0, 0, 0);
     }
     s[0] = f32x16{};
     s[1] = f32x16{};
@@ -423,7 +434,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
       const float m_new = fmaxf(m_ref, mx);
       if (m_new != kNegInf) {  // a row with no visible key yet keeps the empty state
         const float alpha = exp2_fast(m_ref - m_new);  // 0 on the first visible block
-        acc_l *= alpha;
+        acc_l *= __shfl(alpha, l_src, 64);  // the row sums are held in the swapped layout
 #pragma unroll
         for (int i = 0; i < T::DT; ++i) acc[i] *= alpha;
         m_ref = m_new;
@@ -448,7 +459,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
   // asked, the log-sum-exp ln 2 * (m + log2 l): the sum of 2^(s c) is 2^m l for
   // whatever reference m the row ended with ----
   auto store_tile = [&]() __attribute__((always_inline)) {
-    const float l_tot = acc_l[0];
+    const float l_tot = __shfl(acc_l[0], l_src, 64);
     const float inv = 1.0f / l_tot;
     if (Lse && hf == 0 && q < Sq) Lse[(size_t)head * Sq + q] = (m_ref + log2f(l_tot)) * kLn2;
     if (q < Sq) {
@@ -503,16 +514,16 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
           for (int u = 0; u < 2; ++u) pb[t][u] = bf16x8{};
       }
     };
-    // The next tile's Q is waited for right after its load, in the same
-    // branch: the compiler then knows on every path that Q has landed and adds
-    // no waits before the score MFMAs (once per tile, the load latency shows).
+    // The next tile's Q is loaded before this block's weights are formed, so
+    // its latency overlaps the exponentials.  Every softmax phase ends by
+    // waiting for all of this wavefront's loads: the compiler then knows on
+    // every path that Q has landed and adds no waits before the score MFMAs.
+    // (The wait also covers the stage loads issued in the MFMA phase just
+    // ended, three blocks ahead of their use.)
     const int next_q = !finished && jc + 1 == nblk ? tile_index(rc + 1) : -1;
-    if (next_q >= 0) {
-      load_q(next_q);
-      wait_vmcnt<0>();
-    }
+    if (next_q >= 0) load_q(next_q);
     weights();
-    wait_vmcnt<kStageLoads>();
+    wait_vmcnt<0>();
   };
 
   // Global block g at stage P = g mod 4 (g counts the blocks of all this
