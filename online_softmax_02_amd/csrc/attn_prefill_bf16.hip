@@ -431,14 +431,16 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
     mx = pair_max(mx) * c;
     // Move the reference only when the max outgrows it by more than 2^8.
     if (__ballot(mx > m_ref + kRescaleSlack)) {
+      // Every lane takes part (the row sums are held in a layout swapped across
+      // lanes, so the factor travels by a shuffle); a row with no visible key
+      // yet keeps the empty state with a factor of one.
       const float m_new = fmaxf(m_ref, mx);
-      if (m_new != kNegInf) {  // a row with no visible key yet keeps the empty state
-        const float alpha = exp2_fast(m_ref - m_new);  // 0 on the first visible block
-        acc_l *= __shfl(alpha, l_src, 64);  // the row sums are held in the swapped layout
+      const bool empty = m_new == kNegInf;
+      const float alpha = empty ? 1.0f : exp2_fast(m_ref - m_new);  // 0 on the first visible block
+      acc_l *= __shfl(alpha, l_src, 64);
 #pragma unroll
-        for (int i = 0; i < T::DT; ++i) acc[i] *= alpha;
-        m_ref = m_new;
-      }
+      for (int i = 0; i < T::DT; ++i) acc[i] *= alpha;
+      m_ref = empty ? m_ref : m_new;
     }
     const float m_use = m_ref == kNegInf ? 0.f : m_ref;
     // P is rounded to bf16 once; the same rounded values feed the PV MFMA and
