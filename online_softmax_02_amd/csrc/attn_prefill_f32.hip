@@ -65,6 +65,20 @@ __device__ __forceinline__ int v_swz(int row) {
   return CH % 16 == 0 ? ((row >> 2) & 1) << 3 : 0;
 }
 
+// s_waitcnt with vmcnt = N (bits 3:0 and 15:14), expcnt and lgkmcnt not waited on.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+// Wavefront priority 0..3 (an immediate operand, hence the branches; p is uniform).
+__device__ __forceinline__ void set_prio(int p) {
+  if (p >= 3) __builtin_amdgcn_s_setprio(3);
+  else if (p == 2) __builtin_amdgcn_s_setprio(2);
+  else if (p == 1) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 template <int DP, bool NORM>
 __global__ __launch_bounds__(kAttnThreads, 2) void prefill_f32_kernel(
     const float* __restrict__ Qg, const float* __restrict__ Kg, const float* __restrict__ Vg, float* __restrict__ Og,
@@ -106,16 +120,20 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_f32_kernel(
   const __amdgpu_buffer_rsrc_t vr = make_rsrc(Vg + kv_base, (uint32_t)Sk * d * 4);
 
   // Q as the B operand: lane (query l32, half hf) holds d = hf*DP/2 + j.
+  // Issued after the first K block (see the prologue), in the order the
+  // score products consume it.
   float qv[T::HALF];
+  auto load_q = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int j = 0; j < T::HALF; j += 4) {
-    const int col = hf * T::HALF + j;
-    const f32x4 x = buf_ld16f(qr, col < d ? (uint32_t)(q * d + col) * 4 : kOffNowhere);
-    qv[j] = x.x;
-    qv[j + 1] = x.y;
-    qv[j + 2] = x.z;
-    qv[j + 3] = x.w;
-  }
+    for (int j = 0; j < T::HALF; j += 4) {
+      const int col = hf * T::HALF + j;
+      const f32x4 x = buf_ld16f(qr, col < d ? (uint32_t)(q * d + col) * 4 : kOffNowhere);
+      qv[j] = x.x;
+      qv[j + 1] = x.y;
+      qv[j + 2] = x.z;
+      qv[j + 3] = x.w;
+    }
+  };
 
   int wg_row_end = wg_row0 + kRowsPerWave * rs;
   if (wg_row_end > Sq) wg_row_end = Sq;
@@ -266,20 +284,41 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_f32_kernel(
     }
   };
 
-  // Prologue: K and V of the first block, K of the second.  Every slice that
-  // is not empty starts with a visible key for every row.
+  // Prologue: K of the first block, this wavefront's Q rows, V of the first
+  // block and K of the second.  Every slice that is not empty starts with a
+  // visible key for every row.  All workgroups start at once and their first
+  // loads queue behind each other, so the first score products do not wait
+  // for all of them: each wavefront waits for its share of K(jb0) only (loads
+  // complete in issue order), the barrier makes the whole block visible, and
+  // the products then take the Q registers as they arrive (the compiler waits
+  // for each on its first use).  The barrier carries no memory fence, which
+  // would wait for every outstanding load.
   load_k(jb0 * BN, jb0 & 1);
+  load_q();
   load_v(jb0 * BN, jb0 & 1);
   if (jb0 + 1 < nblk) load_k((jb0 + 1) * BN, (jb0 + 1) & 1);
+  wait_vmcnt_le<T::HALF / 4 + T::DMA_PER_WAVE>();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  f32x16 s_cur = qk(jb0 & 1);
+  // The first iteration reads V(jb0) and reloads this K buffer (with block
+  // jb0 + 2): every load has landed and every wavefront has read K(jb0).
   wait_vmem();
   __syncthreads();
-  f32x16 s_cur = qk(jb0 & 1);
-  // The first iteration reloads this K buffer (with block jb0 + 2): every
-  // wavefront must have read it first.
-  __syncthreads();
+  OSX_DEBUG_SYNC_WG();
 
   for (int jb = jb0; jb < nblk; ++jb) {
     const int j0 = jb * BN;
+    // Two workgroups share each CU and, left alone, the older one's
+    // wavefronts win the issue arbitration: it finishes long before the
+    // other, which then runs its remaining blocks with the matrix cores half
+    // idle.  Priority falls with progress (3 for the first quarter of the
+    // slice, down to 0 for the last), so the workgroup that is behind is served
+    // first and the two finish together.
+    set_prio(3 - (4 * (jb - jb0)) / (nblk - jb0));
     const bool has1 = jb + 1 < nblk, has2 = jb + 2 < nblk;
     // K(jb + 2) replaces K(jb) and V(jb + 1) replaces V(jb - 1): both were
     // last read before the previous barrier.
@@ -304,6 +343,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void prefill_f32_kernel(
     }
     wait_vmem();
     __syncthreads();
+    OSX_DEBUG_SYNC_WG();  // nblk is the same for every wavefront of the workgroup
     s_cur = s_next;
   }
 
