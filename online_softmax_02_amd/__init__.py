@@ -9,11 +9,15 @@ importing this package without it raises ``ImportError``.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libosx.so")
+# The same sources built with extra waits and barriers at every LDS stage
+# (see build.py); used by the tests through using_library().
+DEBUG_SYNC_LIB_PATH = os.path.join(_HERE, "libosx_debug_sync.so")
 
 OSX_OK, OSX_EINVAL, OSX_EUNSUPPORTED, OSX_EHIP, OSX_EWORKSPACE = 0, -1, -2, -3, -4
 OSX_F32, OSX_BF16 = 0, 1
@@ -40,7 +44,7 @@ class OsxError(RuntimeError):
         self.status = status
 
 
-def _load() -> ctypes.CDLL:
+def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     # libosx.so links libamdhip64.so.7.  PyTorch ships its own copy of that
     # runtime; loading torch first makes the library bind to the same runtime
     # instead of pulling a second one into the process (two HIP runtimes in one
@@ -49,10 +53,10 @@ def _load() -> ctypes.CDLL:
         import torch  # noqa: F401
     except ImportError:
         pass
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m online_softmax_02_amd.build` "
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m online_softmax_02_amd.build` "
                           "(hipcc for gfx950); there is no fallback implementation")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     attn_shape = [_i, _i, _i, _i, _i, _i, _i, _i]  # dtype, B, Hq, Hkv, Sq, Sk, D, causal
     lib.osx_attn_plan.argtypes = attn_shape + [ctypes.POINTER(Plan)]
     lib.osx_attn_fwd_workspace.argtypes = attn_shape + [ctypes.POINTER(_sz)]
@@ -91,6 +95,19 @@ def _load() -> ctypes.CDLL:
 
 
 lib = _load()
+
+
+@contextlib.contextmanager
+def using_library(path: str):
+    """Route this module's calls through another build of the library (same C
+    ABI, e.g. DEBUG_SYNC_LIB_PATH) until the block ends."""
+    global lib
+    saved = lib
+    lib = _load(path)
+    try:
+        yield lib
+    finally:
+        lib = saved
 
 
 def status_string(status: int) -> str:

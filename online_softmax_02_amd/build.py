@@ -5,6 +5,11 @@
 Objects go to ``online_softmax_02_amd/_build/``; the shared library is written
 next to this file.  ``--asm`` also keeps the gfx950 assembly of every kernel
 file in ``_build/`` for inspection.
+
+Each build also writes ``libosx_debug_sync.so``: the same sources with
+``OSX_DEBUG_SYNC=1``, which adds a full wait and a workgroup barrier at every
+LDS stage boundary (``csrc/common.hpp``).  Its results must equal the default
+library's bit for bit (``tests/test_gpu_debug_sync.py``).
 """
 import os
 import shutil
@@ -17,6 +22,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libosx.so")
+DEBUG_SYNC_LIB = os.path.join(HERE, "libosx_debug_sync.so")
 
 SOURCES = [
     "abi.cpp",
@@ -46,9 +52,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
 
 
-def _compile(src: str, asm: bool) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, asm: bool, build_dir: str, extra: list) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".hip"):
         cmd[1:1] = ["-x", "hip"]
         # Device code only: no value in the kernels is NaN (inputs with NaN are
@@ -58,24 +64,31 @@ def _compile(src: str, asm: bool) -> str:
         cmd += ["-Xarch_device", "-fno-honor-nans"]
     if asm and src.endswith(".hip"):
         cmd += ["--save-temps"]
-    r = subprocess.run(cmd, cwd=BUILD, capture_output=True, text=True)
+    r = subprocess.run(cmd, cwd=build_dir, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile of {src} failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(asm: bool = False, verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def _build_one(lib: str, build_dir: str, extra: list, asm: bool, verbose: bool) -> str:
+    os.makedirs(build_dir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, asm), SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, asm, build_dir, extra), SOURCES))
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {lib}")
+    return lib
+
+
+def build(asm: bool = False, verbose: bool = False) -> str:
+    """Build libosx.so, then libosx_debug_sync.so; returns the first's path."""
+    _build_one(LIB, BUILD, [], asm, verbose)
+    _build_one(DEBUG_SYNC_LIB, os.path.join(BUILD, "debug_sync"), ["-DOSX_DEBUG_SYNC=1"], False, verbose)
     return LIB
 
 

@@ -203,6 +203,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void decode_bf16_kernel(
         *reinterpret_cast<u32x2*>(vt + d * (BN * 2) + ((cc ^ vt_swz(d)) << 4) + 8 * half) = val;
       }
     }
+    OSX_DEBUG_SYNC_WAVE();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -214,6 +215,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void decode_bf16_kernel(
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(vt + d * (BN * 2) + ((grp ^ vt_swz(d)) << 4));
       acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, acc[dt], 0, 0, 0);
     }
+    OSX_DEBUG_SYNC_WAVE();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -257,6 +259,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void decode_bf16_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) accl[(wave * NCOL + l16) * D + 16 * dt + 4 * grp + j] = acc[dt][j];
   __syncthreads();
+  OSX_DEBUG_SYNC_WG();
 
   float* ws_ml = ws;
   const size_t n_part = (size_t)gridDim.x * G;

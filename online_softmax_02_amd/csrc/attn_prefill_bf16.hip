@@ -115,6 +115,7 @@ __device__ __forceinline__ void phase_barrier() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
+  OSX_DEBUG_SYNC_WG();  // every wavefront passes the same number of phase barriers
 }
 
 // D: the kernel's (padded) head dimension, 64 or 128.  PAD: the true head

@@ -29,6 +29,36 @@ __device__ __forceinline__ f32x4 buf_ld16f(__amdgpu_buffer_rsrc_t r, uint32_t by
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maximum): placed where
 // all vector-memory loads are known to be complete, so the compiler's waitcnt
 // analysis does not carry "maybe pending" loads into the next loop iteration.
+// Debug build (OSX_DEBUG_SYNC=1, library libosx_debug_sync.so): an extra full
+// wait (vector memory, LDS and scalar memory) and workgroup barrier at every
+// LDS stage boundary that all wavefronts of a workgroup pass together, and an
+// extra full wait at every wavefront-private LDS stage.  Only the timing
+// changes: the results must equal the default build's bit for bit, and a
+// difference would mean that some stage was read before it was complete, or
+// overwritten while still in use.
+#if defined(OSX_DEBUG_SYNC) && OSX_DEBUG_SYNC
+#define OSX_DEBUG_SYNC_WG()                 \
+  do {                                      \
+    __builtin_amdgcn_sched_barrier(0);      \
+    __builtin_amdgcn_s_waitcnt(0);          \
+    __builtin_amdgcn_s_barrier();           \
+    __builtin_amdgcn_sched_barrier(0);      \
+  } while (0)
+#define OSX_DEBUG_SYNC_WAVE()               \
+  do {                                      \
+    __builtin_amdgcn_sched_barrier(0);      \
+    __builtin_amdgcn_s_waitcnt(0);          \
+    __builtin_amdgcn_sched_barrier(0);      \
+  } while (0)
+#else
+#define OSX_DEBUG_SYNC_WG() \
+  do {                      \
+  } while (0)
+#define OSX_DEBUG_SYNC_WAVE() \
+  do {                        \
+  } while (0)
+#endif
+
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 constexpr float kLog2e = 1.4426950408889634f;

@@ -132,9 +132,11 @@ __device__ __forceinline__ State block_merge(State s, float* sm /* 2*kWaves floa
     sm[2 * wave + 1] = s.l;
   }
   __syncthreads();
+  OSX_DEBUG_SYNC_WG();
   State r = {sm[0], sm[1]};
 #pragma unroll
   for (int w = 1; w < kWaves; ++w) merge_state(r, sm[2 * w], sm[2 * w + 1], k);
+  OSX_DEBUG_SYNC_WG();
   return r;
 }
 
