@@ -59,7 +59,13 @@ int ok() {
   return OSX_OK;
 }
 
-int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+// ceil(a / b) for a >= 0, b > 0, without forming a + b - 1 (which overflows
+// for a near INT64_MAX).
+int64_t cdiv(int64_t a, int64_t b) { return a / b + (a % b != 0); }
+
+// No tensor on one device comes near this (2^47 bytes = 128 TiB against
+// 288 GB of HBM); below it every product the planners form fits in int64.
+constexpr double kMaxTensorBytes = 140737488355328.0;
 
 // Largest of 4, 2, 1 that divides the group size: that many query heads of one
 // KV head share a workgroup; the remaining wavefronts take further row tiles.
@@ -72,7 +78,7 @@ int plan_attn(int dtype, int batch, int heads_q, int heads_kv, int seq_q, int se
   if (batch < 0 || heads_q < 0 || heads_kv < 0 || seq_q < 0 || seq_k < 0 || head_dim < 0)
     return fail(OSX_EINVAL, "negative size (batch=%d heads_q=%d heads_kv=%d seq_q=%d seq_k=%d head_dim=%d)", batch,
                 heads_q, heads_kv, seq_q, seq_k, head_dim);
-  if ((int64_t)batch * heads_q * seq_q == 0) return ok();  // nothing to compute
+  if (batch == 0 || heads_q == 0 || seq_q == 0) return ok();  // nothing to compute
   if (heads_kv == 0 || heads_q % heads_kv != 0)
     return fail(OSX_EINVAL, "heads_q (%d) must be a positive multiple of heads_kv (%d)", heads_q, heads_kv);
   if (seq_k == 0) return fail(OSX_EINVAL, "seq_k == 0 with seq_q > 0: softmax over no keys");
@@ -85,6 +91,10 @@ int plan_attn(int dtype, int batch, int heads_q, int heads_kv, int seq_q, int se
   // 32-bit element offsets: each must stay below 2^31 bytes.
   {
     const int64_t es = dtype == OSX_BF16 ? 2 : 4;
+    const double q_bytes = (double)batch * heads_q * seq_q * head_dim * es;
+    const double kv_bytes = (double)batch * heads_kv * seq_k * head_dim * es;
+    if (q_bytes > kMaxTensorBytes || kv_bytes > kMaxTensorBytes)
+      return fail(OSX_EUNSUPPORTED, "q/o of %.3g bytes or k/v of %.3g bytes: beyond any device", q_bytes, kv_bytes);
     const int64_t longest = (int64_t)(seq_q > seq_k ? seq_q : seq_k) * head_dim * es;
     if (longest >= (1LL << 31))
       return fail(OSX_EUNSUPPORTED, "one head of %lld positions x %d dims is %lld bytes: at most 2^31 - 1",
@@ -146,6 +156,8 @@ int plan_softmax(int64_t rows, int64_t cols, osx_plan* p) {
                                         (long long)cols);
   if (rows == 0) return ok();
   if (cols == 0) return fail(OSX_EINVAL, "cols == 0 with rows > 0: softmax over nothing");
+  if ((double)rows * (double)cols * 4.0 > kMaxTensorBytes)
+    return fail(OSX_EUNSUPPORTED, "%lld x %lld elements: beyond any device", (long long)rows, (long long)cols);
   p->threads = osx::kSoftmaxThreads;
   if (cols <= osx::kSoftmaxWaveMax) {
     p->kernel = OSX_KERNEL_SOFTMAX_WAVE;
@@ -427,6 +439,8 @@ int plan_3pass(int64_t rows, int64_t cols, int method, int* splits, int64_t* gri
   *ws = 0;
   if (rows == 0) return ok();
   if (cols == 0) return fail(OSX_EINVAL, "cols == 0 with rows > 0: softmax over nothing");
+  if ((double)rows * (double)cols * 4.0 > kMaxTensorBytes)
+    return fail(OSX_EUNSUPPORTED, "%lld x %lld elements: beyond any device", (long long)rows, (long long)cols);
   const int64_t sp = cdiv(cols, osx::softmax_3pass_chunk(method));
   if (rows * sp > 0x7fffffff) return fail(OSX_EUNSUPPORTED, "problem needs %lld workgroups", (long long)(rows * sp));
   *splits = (int)sp;

@@ -293,3 +293,18 @@ def test_unfused_comparator_keeps_its_head_dims():
         osx.attn_fwd_unfused_workspace(BF16, 1, 4, 1, 128, 128, 96, True)
     assert e.value.status == osx.OSX_EUNSUPPORTED
     assert osx.attn_fwd_unfused_workspace(BF16, 1, 4, 1, 128, 128, 64, True) > 0
+
+
+def test_plans_beyond_any_device_are_rejected_without_overflow():
+    """Products of int-sized dimensions (here all INT_MAX) exceed int64; the planners reject such shapes from a
+    floating-point size estimate instead of forming the products (found by the sanitized host build)."""
+    big = 2 ** 31 - 1
+    for dtype in (F32, BF16):
+        with pytest.raises(osx.OsxError) as e:
+            osx.attn_plan(dtype, big, big, 1, big, big, 64)
+        assert e.value.status == osx.OSX_EUNSUPPORTED
+        assert osx.lib.osx_attn_fwd_workspace_bytes(dtype, big, big, 1, big, big, 64, 0) == 0
+    with pytest.raises(osx.OsxError) as e:
+        osx.softmax_rows_plan(2 ** 62, 2 ** 62)
+    assert e.value.status == osx.OSX_EUNSUPPORTED
+    assert osx.lib.osx_softmax_rows_workspace_bytes(2 ** 63 - 1, 2 ** 63 - 1) == 0
