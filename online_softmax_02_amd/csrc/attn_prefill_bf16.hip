@@ -201,8 +201,11 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
     q_base = (size_t)head * Sq * d;
   };
   // Does this wavefront's work include block j of its tile?  (Blocks wholly
-  // after its rows do not.)
-  auto visible = [&](int j) { return wave_live && j < nblk && (!cmask || j * BN <= wave_row_last); };
+  // after its rows do not.)  The tests are combined without short-circuit
+  // branches, and the softmax phase marks its rare paths (a tile boundary, the
+  // next tile's Q, a masked block, a rescale) unlikely, so that the common
+  // path falls through with few taken branches.
+  auto visible = [&](int j) { return wave_live & (j < nblk) & (!cmask | (j * BN <= wave_row_last)); };
   // Does block j need the mask for some row of this wavefront?
   auto needs_mask = [&](int j) { return j * BN + BN > Sk || (cmask && j * BN + BN - 1 > row0); };
 
@@ -269,7 +272,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
     return Cursor{r, 0, tile_nblk(idx), tile_kv_base(idx)};
   };
   auto advance = [&](Cursor& cu) __attribute__((always_inline)) {
-    if (++cu.j == cu.nblk && tile_index(cu.r + 1) >= 0) cu = cursor_at(cu.r + 1);
+    if (__builtin_expect(++cu.j == cu.nblk, 0) && tile_index(cu.r + 1) >= 0) cu = cursor_at(cu.r + 1);
   };
   Cursor cur_v = cursor_at(0), cur_k = cursor_at(0);
   // Stage s: V of the block at cursor v and K of the block at cursor k (the
@@ -412,7 +415,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
   // PV on the matrix cores).
   auto softmax = [&](int j) __attribute__((always_inline)) {
     const int j0 = j * BN;
-    if (needs_mask(j)) {
+    if (__builtin_expect(needs_mask(j), 0)) {
       // key j0 + 4hf + o is visible iff o < lim, o = 32t + 8(r/4) + r%4
       int lim = cmask ? (q + 1 < Sk ? q + 1 : Sk) : Sk;
       lim -= j0 + 4 * hf;
@@ -431,7 +434,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
     mx = pair_max(mx) * c;
     // Move the reference only when the max outgrows it by more than 2^8.
-    if (__ballot(mx > m_ref + kRescaleSlack)) {
+    if (__builtin_expect(__ballot(mx > m_ref + kRescaleSlack) != 0, 0)) {
       // Every lane takes part (the row sums are held in a layout swapped across
       // lanes, so the factor travels by a shuffle); a row with no visible key
       // yet keeps the empty state with a factor of one.
@@ -492,7 +495,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
   // the stage two blocks ahead (and for Q, when it was loaded).
   auto softmax_phase = [&](bool next) __attribute__((always_inline)) {
     if (next) {
-      if (jc + 1 < nblk) {
+      if (__builtin_expect(jc + 1 < nblk, 1)) {
         ++jc;
       } else {
         store_tile();
@@ -508,7 +511,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
       }
     }
     auto weights = [&]() __attribute__((always_inline)) {
-      if (!finished && visible(jc)) {
+      if (__builtin_expect(!finished && visible(jc), 1)) {
         softmax(jc);
       } else {
 #pragma unroll
@@ -524,7 +527,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
     // (The wait also covers the stage loads issued in the MFMA phase just
     // ended, three blocks ahead of their use.)
     const int next_q = !finished && jc + 1 == nblk ? tile_index(rc + 1) : -1;
-    if (next_q >= 0) load_q(next_q);
+    if (__builtin_expect(next_q >= 0, 0)) load_q(next_q);
     weights();
     wait_vmcnt<0>();
   };

@@ -28,7 +28,10 @@
 //    use more than one CU.
 //
 // Exponentials are 2^((x - m) * k) with k = scale * log2 e, on the
-// transcendental unit.
+// transcendental unit.  The split-row kernels form the exponent as one FMA,
+// x k - m k, with m k rounded once per thread: its rounding is a factor common
+// to a chunk's sum and to the outputs normalised with the same m, and it saves
+// one vector instruction per element in each pass.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -106,8 +109,9 @@ __device__ __forceinline__ void update(State& s, const float (&v)[N], float k) {
   const float mn = fmaxf(s.m, mb);
   if (mn == kNegInf) return;
   float sum = 0.f;
+  const float mk = mn * k;
 #pragma unroll
-  for (int i = 0; i < N; ++i) sum += exp2_fast((v[i] - mn) * k);
+  for (int i = 0; i < N; ++i) sum += exp2_fast(fmaf(v[i], k, -mk));
   s.l = s.l * exp2_fast((s.m - mn) * k) + sum;
   s.m = mn;
 }
@@ -186,6 +190,7 @@ __device__ __forceinline__ void normalise(const T* __restrict__ x, T* __restrict
   using L = Elem<T>;
   constexpr int E = L::E;
   const int tid = threadIdx.x;
+  const float mk = m * k;
   int64_t tail = begin;
   if (VEC && end > begin) {
     const int64_t nv = (end - begin) / E;
@@ -193,12 +198,12 @@ __device__ __forceinline__ void normalise(const T* __restrict__ x, T* __restrict
       float v[E];
       L::unpack(ld16(x + begin + E * i), v);
 #pragma unroll
-      for (int e = 0; e < E; ++e) v[e] = exp2_fast((v[e] - m) * k) * inv_l;
+      for (int e = 0; e < E; ++e) v[e] = exp2_fast(fmaf(v[e], k, -mk)) * inv_l;
       st16(y + begin + E * i, L::pack(v));
     }
     tail = begin + nv * E;
   }
-  for (int64_t i = tail + tid; i < end; i += kThreads) L::put(y + i, exp2_fast((L::get(x + i) - m) * k) * inv_l);
+  for (int64_t i = tail + tid; i < end; i += kThreads) L::put(y + i, exp2_fast(fmaf(L::get(x + i), k, -mk)) * inv_l);
 }
 
 // Masked columns [begin, end) of a row: y = 0.
@@ -239,21 +244,31 @@ __device__ __forceinline__ State scan_chunk(const T* __restrict__ xb, float k) {
   u32x4 w[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) w[i] = ld16(xb + E * (threadIdx.x + i * kThreads));
-  float m = kNegInf;
+  // Folded in groups of GV vectors, in load order, so the arithmetic on the
+  // first groups runs while the later ones are still arriving.
+  constexpr int GV = NV < 8 ? NV : 8;
+  float m = kNegInf, l = 0.f;
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    float v[E];
-    L::unpack(w[i], v);
+  for (int g0 = 0; g0 < NV; g0 += GV) {
+    float gm = kNegInf;
 #pragma unroll
-    for (int e = 0; e < E; e += 2) m = fmaxf(m, fmaxf(v[e], v[e + 1]));
-  }
-  float l = 0.f;
+    for (int i = g0; i < g0 + GV; ++i) {
+      float v[E];
+      L::unpack(w[i], v);
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    float v[E];
-    L::unpack(w[i], v);
+      for (int e = 0; e < E; e += 2) gm = fmaxf(gm, fmaxf(v[e], v[e + 1]));
+    }
+    const float mn = fmaxf(m, gm);
+    l *= exp2_fast((m - mn) * k);  // 0 for the first group (m = -inf)
+    m = mn;
+    const float mk = m * k;
 #pragma unroll
-    for (int e = 0; e < E; e += 2) l += exp2_fast((v[e] - m) * k) + exp2_fast((v[e + 1] - m) * k);
+    for (int i = g0; i < g0 + GV; ++i) {
+      float v[E];
+      L::unpack(w[i], v);
+#pragma unroll
+      for (int e = 0; e < E; e += 2) l += exp2_fast(fmaf(v[e], k, -mk)) + exp2_fast(fmaf(v[e + 1], k, -mk));
+    }
   }
   return State{m, l};
 }
@@ -266,12 +281,13 @@ __device__ __forceinline__ void normalise_chunk(const T* xb, T* yb, float m, flo
 #pragma unroll
   for (int i = 0; i < NV; ++i)
     w[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xb) + threadIdx.x + i * kThreads);
+  const float mk = m * k;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     float v[E];
     L::unpack(w[i], v);
 #pragma unroll
-    for (int e = 0; e < E; ++e) v[e] = exp2_fast((v[e] - m) * k) * inv_l;
+    for (int e = 0; e < E; ++e) v[e] = exp2_fast(fmaf(v[e], k, -mk)) * inv_l;
     __builtin_nontemporal_store(L::pack(v), reinterpret_cast<u32x4*>(yb) + threadIdx.x + i * kThreads);
   }
 }
