@@ -348,3 +348,27 @@ def test_decode_longest_supported_kv(osx):
     check(to_f64(o)[0, :, 0], want, "bf16", "planted last key")
     assert np.abs(lse.double().cpu().numpy()[0, :, 0] - s_star).max() < 1e-3
     del k, v
+
+
+# ------------------------------------------------------------------ wide GQA groups
+# Query heads per KV head beyond the common 1/2/4/8: G = 16 is the widest group
+# the decode kernel packs into its MFMA columns; G = 32 decode therefore runs
+# the prefill kernel with one query row; G = 6 and 5 give the prefill planner
+# two and one heads per workgroup with several head groups per KV head.
+@pytest.mark.parametrize("case", [
+    # dtype, B, Hq, Hkv, Sq, Sk, d, causal
+    ("bf16", 2, 16, 1, 1, 3000, 128, False),
+    ("bf16", 1, 32, 1, 1, 700, 128, False),
+    ("bf16", 1, 12, 2, 200, 200, 64, True),
+    ("bf16", 2, 10, 2, 130, 130, 128, False),
+    ("f32", 1, 12, 2, 200, 200, 48, True),
+    ("f32", 1, 32, 1, 1, 500, 128, False),
+], ids=lambda c: "-".join(map(str, c)))
+def test_wide_gqa_groups(osx, case):
+    dtype, B, Hq, Hkv, Sq, Sk, d, causal = case
+    print(f"wide GQA {case}", flush=True)
+    t = synth.random_attn(zlib.crc32(str(case).encode()), dtype, B, Hq, Hkv, Sq, Sk, d)
+    plan = osx.attn_plan(osx.OSX_BF16 if dtype == "bf16" else osx.OSX_F32, B, Hq, Hkv, Sq, Sk, d, causal)
+    print(f"  plan {plan['kernel_name']} grid {plan['grid']} heads_per_wg {plan['heads_per_wg']}", flush=True)
+    got = _run_attn(osx, t, dtype, causal)
+    check(got, oracle.attention(t["q"], t["k"], t["v"], causal=causal), dtype, str(case))
