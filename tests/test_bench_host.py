@@ -68,3 +68,14 @@ def test_profile_records_use_the_workload_byte_counts(kernel):
     with open(path) as f:
         rec = json.load(f)
     assert rec["algorithmic_bytes_per_launch"] == int(ALGORITHMIC[kernel])
+
+
+def test_more_than_one_gpu_is_refused_before_any_gpu_work():
+    """One GPU only: --gpus N > 1 exits with status 2 and says so, before importing torch or touching a device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=60)
+    assert r.returncode == 2
+    assert "exactly one GPU" in r.stderr and r.stdout == ""
