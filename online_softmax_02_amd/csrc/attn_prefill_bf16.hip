@@ -365,7 +365,7 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
   auto gemm_fast = [&](const unsigned char* kl, const unsigned char* vl, unsigned char* k_dst,
                        unsigned char* v_dst) __attribute__((always_inline)) {
     constexpr int NQ = 2 * T::KC, NP = 4 * T::DT, N = NQ + NP;
-    constexpr int kAhead = 6, kRing = 8;
+    constexpr int kAhead = 4, kRing = 6;
     auto frag = [&](int m) -> bf16x8 {
       if (m < NQ) return *reinterpret_cast<const bf16x8*>(k_addr(kl, m >> 1, m & 1));
       const int i = m - NQ;
