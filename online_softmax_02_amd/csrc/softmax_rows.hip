@@ -273,14 +273,23 @@ __device__ __forceinline__ State scan_chunk(const T* __restrict__ xb, float k) {
   return State{m, l};
 }
 
+// A whole chunk's 16-byte vectors per thread, loaded by chunk_load and
+// normalised from the registers by normalise_chunk.
 template <typename T>
-__device__ __forceinline__ void normalise_chunk(const T* xb, T* yb, float m, float inv_l, float k) {
-  using L = Elem<T>;
-  constexpr int E = L::E, NV = (int)(kSoftmaxChunk / E / kThreads);
-  u32x4 w[NV];
+constexpr int kChunkVecs = (int)(kSoftmaxChunk / Elem<T>::E / kThreads);
+
+template <typename T>
+__device__ __forceinline__ void chunk_load(const T* xb, u32x4 (&w)[kChunkVecs<T>]) {
 #pragma unroll
-  for (int i = 0; i < NV; ++i)
+  for (int i = 0; i < kChunkVecs<T>; ++i)
     w[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xb) + threadIdx.x + i * kThreads);
+}
+
+template <typename T>
+__device__ __forceinline__ void normalise_chunk(const u32x4 (&w)[kChunkVecs<T>], T* yb, float m, float inv_l,
+                                                float k) {
+  using L = Elem<T>;
+  constexpr int E = L::E, NV = kChunkVecs<T>;
   const float mk = m * k;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
@@ -469,8 +478,9 @@ __global__ __launch_bounds__(kThreads) void softmax_split_pass1(const T* __restr
   }
 }
 
-// Split rows, pass 2: merge the row's partials, then normalise one chunk.
-// Workgroups are dealt to the 8 XCDs round-robin, so chunk id runs on XCD
+// Split rows, pass 2: merge the row's partials, then normalise one chunk.  A
+// whole chunk's loads are issued first, so they are in flight while the
+// partials are read and merged.  Workgroups are dealt to the 8 XCDs round-robin, so chunk id runs on XCD
 // id mod 8 in both passes; pass 2 walks each XCD's chunks in reverse, so it
 // starts with the chunks pass 1 read last, which are still in that XCD's L2
 // (2% faster on a 2^24-element row than the same order).
@@ -484,16 +494,19 @@ __global__ __launch_bounds__(kThreads) void softmax_split_pass2(const T* x, T* y
       nwg % 8 == 0 ? (nwg / 8 - 1 - (int64_t)blockIdx.x / 8) * 8 + blockIdx.x % 8 : (int64_t)blockIdx.x;
   const int64_t row = id / splits;
   const int64_t ck = id - row * splits;
-  State s = {kNegInf, 0.f};
-  const float* pr = part + 2 * row * splits;
-  for (int i = threadIdx.x; i < splits; i += kThreads) merge_state(s, pr[2 * i], pr[2 * i + 1], k);
-  s = block_merge(s, sm, k);
   const int64_t lim = row_limit(row, cols, period);
   const int64_t begin = ck * chunk;
   const int64_t end = begin + chunk < cols ? begin + chunk : cols;
   const int64_t vis = end < lim ? end : lim;
-  if (VEC && vis - begin == kSoftmaxChunk)
-    normalise_chunk(x + row * cols + begin, y + row * cols + begin, s.m, 1.0f / s.l, k);
+  const bool whole = VEC && vis - begin == kSoftmaxChunk;  // uniform across the workgroup
+  u32x4 w[kChunkVecs<T>];
+  if (whole) chunk_load(x + row * cols + begin, w);
+  State s = {kNegInf, 0.f};
+  const float* pr = part + 2 * row * splits;
+  for (int i = threadIdx.x; i < splits; i += kThreads) merge_state(s, pr[2 * i], pr[2 * i + 1], k);
+  s = block_merge(s, sm, k);
+  if (whole)
+    normalise_chunk(w, y + row * cols + begin, s.m, 1.0f / s.l, k);
   else
     normalise<T, VEC>(x + row * cols, y + row * cols, begin, vis, s.m, 1.0f / s.l, k);
   zero_fill<T, VEC>(y + row * cols, vis > begin ? vis : begin, end);
