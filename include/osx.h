@@ -16,9 +16,13 @@
  *
  * Conventions for every entry point:
  *   - Pointers q, k, v, o, x, y, workspace are DEVICE pointers owned by the
- *     caller; the library allocates no device memory, keeps no pointer after
- *     it returns and has no global mutable state besides a thread-local error
- *     message.
+ *     caller; the library allocates no device memory and keeps no pointer
+ *     after it returns.  Its only global state: a thread-local error message,
+ *     a per-device cache of the compute-unit count, and the static scratch of
+ *     osx_attn_fwd_noalloc with its per-device address.
+ *   - Every call works on the calling thread's current HIP device: the
+ *     buffers must be that device's memory, `stream` must belong to it, and
+ *     the planners size their grids by its compute-unit count.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *     asynchronously on it; nothing synchronises the device.  Buffers must stay
  *     alive until that work has finished.

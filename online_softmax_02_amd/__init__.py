@@ -160,6 +160,25 @@ def _torch():
     return torch
 
 
+def _common_device(*tensors, stream=None):
+    """The one device of the tensors (None entries skipped); ValueError when they, or a torch stream given for
+    them, are on different devices."""
+    torch = _torch()
+    devs = {t.device for t in tensors if t is not None}
+    if len(devs) != 1:
+        raise ValueError("the tensors of one call must be on one CUDA device, got " + ", ".join(sorted(map(str, devs))))
+    dev = devs.pop()
+    if isinstance(stream, torch.cuda.Stream) and stream.device != dev:
+        raise ValueError(f"the stream belongs to {stream.device}, the tensors to {dev}")
+    return dev
+
+
+def _device_of(*tensors, stream=None):
+    """Context in which the tensors' common device is current: the C ABI plans and launches on the current
+    device."""
+    return _torch().cuda.device(_common_device(*tensors, stream=stream))
+
+
 def _stream(t, stream):
     torch = _torch()
     if stream is None:
@@ -202,8 +221,9 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}: float32 or bfloat16")
 
 
-def _attn_prepare(q, k, v, causal, out, workspace):
-    """Checks q, k, v and out, allocates what is missing; returns the 4-D views and the call arguments."""
+def _attn_prepare(q, k, v, causal, out, workspace, stream=None):
+    """Checks q, k, v and out, allocates what is missing (on q's device); returns the 4-D views and the call
+    arguments."""
     torch = _torch()
     squeeze = q.dim() == 2
     if squeeze:
@@ -222,12 +242,13 @@ def _attn_prepare(q, k, v, causal, out, workspace):
     if Bk != B or Dk != D:
         raise ValueError("batch and head_dim of q and k must match")
     code = _dtype_code(q)
-    if out is None:
-        out = torch.empty_like(q)
-    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+    if out is not None and (out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous()):
         raise ValueError("out must be a contiguous tensor like q")
-    need = attn_fwd_workspace(code, B, Hq, Hkv, Sq, Sk, D, causal)
-    ws = _workspace(need, workspace, q.device)
+    with _device_of(q, k, v, out, workspace, stream=stream):
+        if out is None:
+            out = torch.empty_like(q)
+        need = attn_fwd_workspace(code, B, Hq, Hkv, Sq, Sk, D, causal)
+        ws = _workspace(need, workspace, q.device)
     return squeeze, q, k, v, out, code, (B, Hq, Hkv, Sq, Sk, D), ws
 
 
@@ -251,16 +272,18 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None
     ``return_lse`` also the float32 [B, Hq, Sq] (or [M]) log-sum-exp of each
     row's scaled, masked scores (``lse`` may supply that tensor).
     """
-    squeeze, q, k, v, out, code, shape, (ws, ws_ptr, ws_len) = _attn_prepare(q, k, v, causal, out, workspace)
+    squeeze, q, k, v, out, code, shape, (ws, ws_ptr, ws_len) = _attn_prepare(q, k, v, causal, out, workspace, stream)
     sc = float(scale) if scale else 0.0
     if not (return_lse or lse is not None):
-        _check(lib.osx_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), code, *shape, int(causal),
-                                sc, ws_ptr, ws_len, _stream(q, stream)))
+        with _device_of(q, k, v, out, ws, stream=stream):
+            _check(lib.osx_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), code, *shape,
+                                    int(causal), sc, ws_ptr, ws_len, _stream(q, stream)))
         _hold(ws if workspace is None else None, stream)
         return out[0, 0] if squeeze else out
     lse = _lse_tensor(q, shape, lse)
-    _check(lib.osx_attn_fwd_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), code, *shape,
-                                int(causal), sc, ws_ptr, ws_len, _stream(q, stream)))
+    with _device_of(q, k, v, out, ws, lse, stream=stream):
+        _check(lib.osx_attn_fwd_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), code,
+                                    *shape, int(causal), sc, ws_ptr, ws_len, _stream(q, stream)))
     _hold(ws if workspace is None else None, stream)
     if squeeze:
         return out[0, 0], lse.reshape(-1)
@@ -270,14 +293,15 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None
 def attn_fwd_normalised(q, k, v, causal: bool = False, scale: float | None = None, out=None, workspace=None,
                         stream=None, return_lse: bool = False, lse=None):
     """attn_fwd computed with the normalised-output recurrence (osx_attn_fwd_normalised): float32 only."""
-    squeeze, q, k, v, out, code, shape, (ws, ws_ptr, ws_len) = _attn_prepare(q, k, v, causal, out, workspace)
+    squeeze, q, k, v, out, code, shape, (ws, ws_ptr, ws_len) = _attn_prepare(q, k, v, causal, out, workspace, stream)
     sc = float(scale) if scale else 0.0
     want = return_lse or lse is not None
     if want:
         lse = _lse_tensor(q, shape, lse)
-    _check(lib.osx_attn_fwd_normalised(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                       lse.data_ptr() if want else None, code, *shape, int(causal), sc, ws_ptr, ws_len,
-                                       _stream(q, stream)))
+    with _device_of(q, k, v, out, ws, lse if want else None, stream=stream):
+        _check(lib.osx_attn_fwd_normalised(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                           lse.data_ptr() if want else None, code, *shape, int(causal), sc, ws_ptr,
+                                           ws_len, _stream(q, stream)))
     _hold(ws if workspace is None else None, stream)
     o = out[0, 0] if squeeze else out
     if not want:
@@ -306,9 +330,10 @@ def attn_fwd_noalloc(q, k, v, out, causal: bool = False, scale: float | None = N
     if lse is not None and (lse.numel() != B * Hq * Sq or not lse.is_contiguous()
                             or lse.dtype != _torch().float32):
         raise ValueError("lse must be a contiguous float32 tensor of B * Hq * Sq elements")
-    _check(lib.osx_attn_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                    lse.data_ptr() if lse is not None else None, _dtype_code(q), B, Hq, Hkv, Sq, Sk,
-                                    D, int(causal), float(scale) if scale else 0.0, _stream(q, stream)))
+    with _device_of(q, k, v, out, lse, stream=stream):
+        _check(lib.osx_attn_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                        lse.data_ptr() if lse is not None else None, _dtype_code(q), B, Hq, Hkv, Sq,
+                                        Sk, D, int(causal), float(scale) if scale else 0.0, _stream(q, stream)))
     return out[0, 0] if squeeze else out
 
 
@@ -328,12 +353,14 @@ def softmax_rows(x, out=None, workspace=None, stream=None, causal_period: int = 
         out = torch.empty_like(x)
     elif out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous():
         raise ValueError("out must be a contiguous tensor like x")
-    ws, ws_ptr, ws_len = _workspace(softmax_rows_workspace(rows, cols), workspace, x.device)
-    if x.dtype == torch.float32 and not causal_period and scale == 1.0:
-        _check(lib.osx_softmax_rows(x.data_ptr(), out.data_ptr(), rows, cols, ws_ptr, ws_len, _stream(x, stream)))
-    else:
-        _check(lib.osx_softmax_rows_ex(x.data_ptr(), out.data_ptr(), _dtype_code(x), rows, cols, int(causal_period),
-                                       float(scale), ws_ptr, ws_len, _stream(x, stream)))
+    with _device_of(x, out, workspace, stream=stream):
+        ws, ws_ptr, ws_len = _workspace(softmax_rows_workspace(rows, cols), workspace, x.device)
+        if x.dtype == torch.float32 and not causal_period and scale == 1.0:
+            _check(lib.osx_softmax_rows(x.data_ptr(), out.data_ptr(), rows, cols, ws_ptr, ws_len,
+                                        _stream(x, stream)))
+        else:
+            _check(lib.osx_softmax_rows_ex(x.data_ptr(), out.data_ptr(), _dtype_code(x), rows, cols,
+                                           int(causal_period), float(scale), ws_ptr, ws_len, _stream(x, stream)))
     _hold(ws if workspace is None else None, stream)
     return out
 
@@ -367,11 +394,12 @@ def attn_fwd_unfused(q, k, v, causal: bool = False, scale: float | None = None, 
         out = torch.empty_like(q)
     elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
         raise ValueError("out must be a contiguous tensor like q")
-    ws, ws_ptr, ws_len = _workspace(attn_fwd_unfused_workspace(code, B, Hq, Hkv, Sq, Sk, D, causal), workspace,
-                                    q.device)
-    _check(lib.osx_attn_fwd_unfused(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), code, B, Hq, Hkv, Sq,
-                                    Sk, D, int(causal), float(scale) if scale else 0.0, ws_ptr, ws_len,
-                                    _stream(q, stream)))
+    with _device_of(q, k, v, out, workspace, stream=stream):
+        ws, ws_ptr, ws_len = _workspace(attn_fwd_unfused_workspace(code, B, Hq, Hkv, Sq, Sk, D, causal), workspace,
+                                        q.device)
+        _check(lib.osx_attn_fwd_unfused(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), code, B, Hq, Hkv,
+                                        Sq, Sk, D, int(causal), float(scale) if scale else 0.0, ws_ptr, ws_len,
+                                        _stream(q, stream)))
     _hold(ws if workspace is None else None, stream)
     return out[0, 0] if squeeze else out
 
@@ -398,9 +426,10 @@ def softmax_rows_3pass(x, method: int, out=None, workspace=None, stream=None):
         out = torch.empty_like(x)
     elif out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous():
         raise ValueError("out must be a contiguous tensor like x")
-    ws, ws_ptr, ws_len = _workspace(softmax_rows_3pass_workspace(rows, cols, method), workspace, x.device)
-    _check(lib.osx_softmax_rows_3pass(x.data_ptr(), out.data_ptr(), rows, cols, method, ws_ptr, ws_len,
-                                      _stream(x, stream)))
+    with _device_of(x, out, workspace, stream=stream):
+        ws, ws_ptr, ws_len = _workspace(softmax_rows_3pass_workspace(rows, cols, method), workspace, x.device)
+        _check(lib.osx_softmax_rows_3pass(x.data_ptr(), out.data_ptr(), rows, cols, method, ws_ptr, ws_len,
+                                          _stream(x, stream)))
     _hold(ws if workspace is None else None, stream)
     return out
 
@@ -415,8 +444,9 @@ def read_probe(x, sink=None, stream=None):
     nbytes = x.numel() * x.element_size()
     if sink is None:
         sink = torch.empty(lib.osx_read_probe_sink_bytes() // 4, dtype=torch.int32, device=x.device)
-    _check(lib.osx_read_probe(x.data_ptr(), nbytes, sink.data_ptr(), sink.numel() * sink.element_size(),
-                              _stream(x, stream)))
+    with _device_of(x, sink, stream=stream):
+        _check(lib.osx_read_probe(x.data_ptr(), nbytes, sink.data_ptr(), sink.numel() * sink.element_size(),
+                                  _stream(x, stream)))
     return sink
 
 

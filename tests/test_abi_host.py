@@ -308,3 +308,10 @@ def test_plans_beyond_any_device_are_rejected_without_overflow():
         osx.softmax_rows_plan(2 ** 62, 2 ** 62)
     assert e.value.status == osx.OSX_EUNSUPPORTED
     assert osx.lib.osx_softmax_rows_workspace_bytes(2 ** 63 - 1, 2 ** 63 - 1) == 0
+
+
+def test_tensors_of_one_call_must_share_a_device():
+    import torch
+    with pytest.raises(ValueError, match="one CUDA device"):
+        osx._common_device(torch.empty(1), torch.empty(1, device="meta"))
+    assert osx._common_device(torch.empty(1), None, torch.empty(2)) == torch.device("cpu")
