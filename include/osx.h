@@ -131,7 +131,8 @@ size_t osx_attn_fwd_workspace_bytes(int dtype, int batch, int heads_q, int heads
  * 1/sqrt(head_dim) (page "softmax_attention": scores are multiplied by
  * d^-0.5).  workspace: device buffer of at least the bytes
  * osx_attn_fwd_workspace reports (may be NULL when that is 0); its contents
- * on entry do not matter.  o must not overlap q, k, v or the workspace.
+ * on entry do not matter.  o must not overlap q, k, v or the workspace, nor
+ * the workspace q, k or v (OSX_EINVAL).
  */
 int osx_attn_fwd(const void* q, const void* k, const void* v, void* o, int dtype, int batch, int heads_q,
                  int heads_kv, int seq_q, int seq_k, int head_dim, int causal, float scale, void* workspace,

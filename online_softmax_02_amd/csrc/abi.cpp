@@ -281,6 +281,9 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, b
   if (overlap(o, nq, q, nq) || overlap(o, nq, k, nkv) || overlap(o, nq, v, nkv) ||
       (p.workspace_bytes && overlap(o, nq, workspace, p.workspace_bytes)))
     return fail(OSX_EINVAL, "output overlaps an input or the workspace");
+  if (p.workspace_bytes && (overlap(workspace, p.workspace_bytes, q, nq) || overlap(workspace, p.workspace_bytes, k, nkv) ||
+                            overlap(workspace, p.workspace_bytes, v, nkv)))
+    return fail(OSX_EINVAL, "workspace overlaps q, k or v");
   if (lse) {
     const size_t nl = (size_t)batch * heads_q * seq_q * sizeof(float);
     if (overlap(lse, nl, q, nq) || overlap(lse, nl, k, nkv) || overlap(lse, nl, v, nkv) || overlap(lse, nl, o, nq) ||

@@ -73,6 +73,11 @@ def test_attn_fwd_rejects_before_launch():
     st = lib.osx_attn_fwd(fake, ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000), fake,
                           F32, 1, 1, 1, 16, 16, 64, 0, 0.0, None, 0, None)
     assert st == osx.OSX_EINVAL and "overlap" in osx.last_error()
+    # a workspace over the keys: the partial states would overwrite K
+    need = osx.attn_fwd_workspace(BF16, 1, 4, 1, 1, 8192, 128)
+    st = lib.osx_attn_fwd(fake, ctypes.c_void_p(0x100000), ctypes.c_void_p(0x800000), ctypes.c_void_p(0x1000000),
+                          BF16, 1, 4, 1, 1, 8192, 128, 0, 0.0, ctypes.c_void_p(0x100000 + 4096), need, None)
+    assert st == osx.OSX_EINVAL and "workspace overlaps" in osx.last_error()
 
 
 def test_softmax_rejects_before_launch():
