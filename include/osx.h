@@ -21,8 +21,9 @@
  *     a per-device cache of the compute-unit count, and the static scratch of
  *     osx_attn_fwd_noalloc with its per-device address.
  *   - Every call works on the calling thread's current HIP device: the
- *     buffers must be that device's memory, `stream` must belong to it, and
- *     the planners size their grids by its compute-unit count.
+ *     buffers must be that device's memory and `stream` must belong to it
+ *     (the bf16 prefill sizes its persistent grid by that device's
+ *     compute-unit count).  The plan and workspace queries make no HIP call.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *     asynchronously on it; nothing synchronises the device.  Buffers must stay
  *     alive until that work has finished.

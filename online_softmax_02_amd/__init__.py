@@ -174,8 +174,7 @@ def _common_device(*tensors, stream=None):
 
 
 def _device_of(*tensors, stream=None):
-    """Context in which the tensors' common device is current: the C ABI plans and launches on the current
-    device."""
+    """Context in which the tensors' common device is current: the C ABI launches on the current device."""
     return _torch().cuda.device(_common_device(*tensors, stream=stream))
 
 
