@@ -305,11 +305,21 @@ __global__ __launch_bounds__(kAttnThreads, 2) void decode_bf16_kernel(
   }
 }
 
-// Merge the splits of one (batch, query head): O = sum acc_s 2^(m_s-m) / sum l_s 2^(m_s-m).
-// One thread per output column: the launch has d threads.
+// Merge the splits of one (batch, query head): with M = max_s m_s,
+// O = sum_s acc_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).  One thread per output
+// column (the launch has d threads).  Every load is unconditional (indices
+// past the last split are clamped to it and weighted 0), so the (m, l) pairs
+// of all splits, staged in LDS, and each column's first kBatch accumulator
+// values are in flight together: up to kBatch splits cost one memory round
+// trip, where loads guarded per split went out one after another.  The launch
+// takes the smallest kBatch that covers the splits (64 beyond that), so few
+// splits issue few redundant loads.
+template <int kBatch>
 __global__ __launch_bounds__(128) void decode_combine_kernel(const float* __restrict__ ws, uint16_t* __restrict__ Og,
                                                              float* __restrict__ Lse, int Hq, int Hkv, int splits,
                                                              int n_wg, int D) {
+  __shared__ __align__(16) float sm_m[kDecodeMaxSplits];
+  __shared__ float sm_l[kDecodeMaxSplits];
   const int bh = blockIdx.x;
   const int b = bh / Hq, hq = bh % Hq;
   const int G = Hq / Hkv;
@@ -319,35 +329,36 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const float* __rest
   const float* ws_ml = ws;
   const float* ws_acc = ws + 2 * n_part;
   const int dd = threadIdx.x;
-  // One pass over the splits in batches of 8, each batch's loads issued before
-  // any is used; the running (M, l, a) absorbs a batch with the same rule.
-  constexpr int kBatch = 8;
-  float M = kNegInf, l = 0.f, a = 0.f;
+  auto part = [&](int sp) { return (size_t)(bkv * splits + sp) * G + g; };
+  float as[kBatch];
+#pragma unroll
+  for (int i = 0; i < kBatch; ++i) as[i] = ws_acc[part(min(i, splits - 1)) * D + dd];
+  const int padded = (splits + 3) & ~3;
+  for (int sp = dd; sp < padded; sp += blockDim.x) {
+    float2 ml = {kNegInf, 0.f};  // the padding: an empty split
+    if (sp < splits) ml = *reinterpret_cast<const float2*>(ws_ml + part(sp) * 2);
+    sm_m[sp] = ml.x;
+    sm_l[sp] = ml.y;
+  }
+  __syncthreads();
+  float M = kNegInf;
+  for (int sp = 0; sp < padded; sp += 4) {
+    const float4 m4 = *reinterpret_cast<const float4*>(sm_m + sp);
+    M = fmaxf(M, fmaxf(fmaxf(m4.x, m4.y), fmaxf(m4.z, m4.w)));
+  }
+  float l = 0.f, a = 0.f;
   for (int s0 = 0; s0 < splits; s0 += kBatch) {
-    float ms[kBatch], ls[kBatch], as[kBatch];
+    if (s0 > 0) {
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const bool in = s0 + b < splits;
-      const size_t p = (size_t)(bkv * splits + (in ? s0 + b : s0)) * G + g;
-      ms[b] = in ? ws_ml[p * 2] : kNegInf;
-      ls[b] = in ? ws_ml[p * 2 + 1] : 0.f;
-      as[b] = in ? ws_acc[p * D + dd] : 0.f;
+      for (int i = 0; i < kBatch; ++i) as[i] = ws_acc[part(min(s0 + i, splits - 1)) * D + dd];
     }
-    float mb = ms[0];
 #pragma unroll
-    for (int b = 1; b < kBatch; ++b) mb = fmaxf(mb, ms[b]);
-    const float mn = fmaxf(M, mb);
-    if (mn == kNegInf) continue;  // no key seen yet
-    const float r = exp2_fast(M - mn);  // 0 while M is -inf
-    l *= r;
-    a *= r;
-#pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const float f = exp2_fast(ms[b] - mn);  // 0 for an empty or missing split
-      l += ls[b] * f;
-      a += as[b] * f;
+    for (int i = 0; i < kBatch; ++i) {
+      const int sp = min(s0 + i, splits - 1);
+      const float f = s0 + i < splits ? exp2_fast(sm_m[sp] - M) : 0.f;  // 0 for an empty split (m = -inf)
+      l += sm_l[sp] * f;
+      a += as[i] * f;
     }
-    M = mn;
   }
   const float o = a / l;
   // log sum_j exp(scale * s_j) = ln 2 * (M + log2 l), M in the log2 domain
@@ -368,9 +379,14 @@ hipError_t launch(const AttnArgs& a) {
                      a.seq_k, a.head_dim, a.c, splits, kps);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)(a.batch * a.heads_q)), dim3((unsigned)a.head_dim), 0,
-                     a.stream, ws, static_cast<uint16_t*>(a.o), a.lse, a.heads_q, a.heads_kv, splits, (int)a.plan.grid,
-                     a.head_dim);
+  if (splits > kDecodeMaxSplits) return hipErrorInvalidValue;  // beyond the combine's LDS staging
+  auto combine = splits <= 4    ? decode_combine_kernel<4>
+                 : splits <= 8  ? decode_combine_kernel<8>
+                 : splits <= 16 ? decode_combine_kernel<16>
+                 : splits <= 32 ? decode_combine_kernel<32>
+                                : decode_combine_kernel<64>;
+  hipLaunchKernelGGL(combine, dim3((unsigned)(a.batch * a.heads_q)), dim3((unsigned)a.head_dim), 0, a.stream, ws,
+                     static_cast<uint16_t*>(a.o), a.lse, a.heads_q, a.heads_kv, splits, (int)a.plan.grid, a.head_dim);
   return hipGetLastError();
 }
 

@@ -21,6 +21,7 @@ constexpr int kF32BlockN = 32;        // keys per LDS block, fp32 prefill
 constexpr int kDecodeBlockN = 32;     // keys per wavefront step, decode
 constexpr int kDecodeMaxGroup = 16;   // query heads per KV head the decode kernel can pack
 constexpr int kDecodeTargetWgs = 512;
+constexpr int kDecodeMaxSplits = kDecodeTargetWgs;  // splits = ceil(target / units) <= target
 constexpr int kSplitTargetWgs = 512;   // fp32 prefill: split the keys below this many workgroups
 constexpr int kSplitMinBlocks = 4;     // ... keeping at least this many key blocks per slice
 constexpr int kSoftmaxThreads = 256;
