@@ -350,6 +350,27 @@ def test_decode_longest_supported_kv(osx):
     del k, v
 
 
+@pytest.mark.parametrize("case", [
+    # B, Hq, Hkv, Sk, d -> key splits of the plan
+    (1, 16, 1, 131072, 64),   # 512 splits, the planner's largest: 8 batches of the combine
+    (1, 4, 1, 40000, 128),    # 313 splits: a count that is not a multiple of the combine's batch
+], ids=lambda c: "-".join(map(str, c)))
+def test_decode_most_splits_against_the_oracle(osx, case):
+    """Decode whose keys are split the most the planner does (one (batch, KV head) unit), compared in full with
+    the oracle, output and log-sum-exp: every split's partial state enters the combine."""
+    B, Hq, Hkv, Sk, d = case
+    plan = osx.attn_plan(osx.OSX_BF16, B, Hq, Hkv, 1, Sk, d)
+    print(f"case decode most splits {case}: {plan['splits']} splits", flush=True)
+    assert plan["splits"] == min(512, -(-Sk // 128))
+    t = synth.random_attn(zlib.crc32(str(case).encode()), "bf16", B, Hq, Hkv, 1, Sk, d)
+    q, k, v = to_dev(t["q"]), to_dev(t["k"]), to_dev(t["v"])
+    o, lse = osx.attn_fwd(q, k, v, return_lse=True)
+    torch.cuda.synchronize()
+    check(to_f64(o), oracle.attention(t["q"], t["k"], t["v"]), "bf16", str(case))
+    lerr = np.abs(lse.double().cpu().numpy() - oracle.attention_lse(t["q"], t["k"])).max()
+    assert lerr <= LSE_BF16_ATOL, f"{case}: lse error {lerr:.3e}"
+
+
 # ------------------------------------------------------------------ wide GQA groups
 # Query heads per KV head beyond the common 1/2/4/8: G = 16 is the widest group
 # the decode kernel packs into its MFMA columns; G = 32 decode therefore runs
