@@ -22,10 +22,11 @@
 //  * rows up to kSoftmaxRowMax elements: the same with one workgroup per row,
 //    merged through LDS (the pages keep (m, l) inside one program);
 //  * longer rows: the row is cut into kSoftmaxChunk-element chunks, one
-//    workgroup each.  Pass 1 writes one (m, l) partial per chunk; pass 2 merges
-//    a row's partials with the same rescaling rule, then reads its chunk again
-//    and normalises it.  This replaces the single-program scan, which cannot
-//    use more than one CU.
+//    workgroup each.  Pass 1 writes one (m, l) partial per chunk; pass 2
+//    issues the loads of its chunk (x read again), merges the row's partials
+//    with the same rescaling rule while they are in flight, then normalises
+//    the chunk.  This replaces the single-program scan, which cannot use more
+//    than one CU.
 //
 // Exponentials are 2^((x - m) * k) with k = scale * log2 e, on the
 // transcendental unit.  The split-row kernels form the exponent as one FMA,
