@@ -468,18 +468,30 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void prefill_bf16_kernel(
     const float l_tot = __shfl(acc_l[0], l_src, 64);
     const float inv = 1.0f / l_tot;
     if (Lse && hf == 0 && q < Sq) Lse[(size_t)head * Sq + q] = (m_ref + log2f(l_tot)) * kLn2;
-    if (q < Sq) {
-      uint16_t* op = Og + q_base + (size_t)q * d;
+    // Lane (query q, half hf) holds, per 32-row tile dt and group g, columns
+    // 32 dt + 8 g + 4 hf .. +3 of its row.  One v_permlane32_swap per word
+    // (with every lane active) trades the two halves' pieces so that each lane
+    // holds 8 consecutive columns -- hf = 0 those of groups 2k, hf = 1 those of
+    // groups 2k + 1 -- and writes them as one 16-byte store: half the store
+    // instructions and requests of 8-byte pieces.
+    uint16_t* op = Og + q_base + (size_t)q * d;
 #pragma unroll
-      for (int dt = 0; dt < T::DT; ++dt)
+    for (int dt = 0; dt < T::DT; ++dt)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d0 = 32 * dt + 8 * g + 4 * hf;
-          const u32x2 w = {pack_bf16x2(acc[dt][4 * g] * inv, acc[dt][4 * g + 1] * inv),
-                           pack_bf16x2(acc[dt][4 * g + 2] * inv, acc[dt][4 * g + 3] * inv)};
-          if (d0 < d) *reinterpret_cast<u32x2*>(op + d0) = w;  // padded columns are not stored
+      for (int k = 0; k < 2; ++k) {
+        u32x4 w;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t ev = pack_bf16x2(acc[dt][8 * k + 2 * h] * inv, acc[dt][8 * k + 2 * h + 1] * inv);
+          const uint32_t od = pack_bf16x2(acc[dt][8 * k + 4 + 2 * h] * inv, acc[dt][8 * k + 5 + 2 * h] * inv);
+          // the upper half's even-group word for the lower half's odd-group word
+          const auto r = __builtin_amdgcn_permlane32_swap(ev, od, false, false);
+          w[h] = r[0];      // hf = 0: its own columns 16k + 2h ..; hf = 1: the partner's 16k + 8 + 2h ..
+          w[2 + h] = r[1];  // hf = 0: the partner's columns 16k + 4 + 2h ..; hf = 1: its own 16k + 12 + 2h ..
         }
-    }
+        const int d0 = 32 * dt + 16 * k + 8 * hf;
+        if (q < Sq && d0 < d) *reinterpret_cast<u32x4*>(op + d0) = w;  // padded columns are not stored
+      }
   };
 
   // The block the next softmax phase handles: block jc of tile rc (ordinal
