@@ -23,7 +23,7 @@ constexpr int kDecodeMaxGroup = 16;   // query heads per KV head the decode kern
 constexpr int kDecodeTargetWgs = 512;
 constexpr int kDecodeMaxSplits = kDecodeTargetWgs;  // splits = ceil(target / units) <= target
 constexpr int kSplitTargetWgs = 512;   // fp32 prefill: split the keys below this many workgroups
-constexpr int kSplitMinBlocks = 4;     // ... keeping at least this many key blocks per slice
+constexpr int kSplitMinBlocks = 2;     // ... keeping at least this many key blocks per slice
 constexpr int kSoftmaxThreads = 256;
 constexpr int64_t kSoftmaxWaveMax = 2048;  // longest row held by one wavefront (32 elements per lane)
 constexpr int64_t kSoftmaxRowMax = 8192;   // longest row held by one workgroup (32 elements per thread)
