@@ -320,3 +320,22 @@ def test_tensors_of_one_call_must_share_a_device():
     with pytest.raises(ValueError, match="one CUDA device"):
         osx._common_device(torch.empty(1), torch.empty(1, device="meta"))
     assert osx._common_device(torch.empty(1), None, torch.empty(2)) == torch.device("cpu")
+
+
+@pytest.mark.parametrize("shape,splits", [
+    # (B, Hq, Hkv, Sq, Sk, d, causal) -> key slices of the fp32 plan
+    ((1, 1, 1, 64, 100, 48, 0), 1),        # four 32-key blocks would leave slices under two blocks: no split
+    ((1, 1, 1, 64, 127, 48, 0), 1),
+    ((1, 1, 1, 64, 128, 48, 0), 2),        # two slices of two blocks
+    ((1, 1, 1, 64, 1000, 48, 0), 15),      # floor(1000 / 64) slices of at least two blocks
+    ((1, 1, 1, 256, 512, 128, 0), 8),
+    ((1, 1, 1, 4096, 4096, 128, 0), 16),   # 32 row tiles x 16 slices = 512 workgroups, the target
+    ((1, 4, 4, 128, 4096, 128, 0), 64),    # the combine's limit: one lane per slice
+])
+def test_f32_key_slices_hold_at_least_two_blocks(shape, splits):
+    p = osx.attn_plan(F32, *shape)
+    assert p["splits"] == splits, (shape, p)
+    assert shape[4] >= splits * 64 or splits == 1
+    if splits > 1:
+        B, Hq, Hkv, Sq, Sk, d, causal = shape
+        assert p["workspace_bytes"] == B * Hq * Sq * splits * (2 + d) * 4
