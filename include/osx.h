@@ -35,7 +35,8 @@
  *   - Arguments are checked on the host before anything is launched.  On error
  *     nothing is launched and a negative status is returned; osx_last_error()
  *     then describes the failure.  A call with no work (an empty batch, zero
- *     query rows, zero rows or columns) returns OSX_OK and launches nothing.
+ *     query rows, zero softmax rows) returns OSX_OK and launches nothing; a
+ *     softmax over zero columns of a non-empty row is OSX_EINVAL.
  *   - With OSX_LOG=1 in the environment (read once per process) every call of
  *     osx_attn_fwd* and osx_softmax_rows* that launches work prints one line on
  *     stderr: the problem and the kernel, grid and workspace the plan chose.
@@ -52,7 +53,8 @@ extern "C" {
 
 /* Status codes. */
 #define OSX_OK 0
-#define OSX_EINVAL (-1)      /* bad argument: null pointer, negative size, Hq % Hkv != 0, empty softmax, overlap */
+#define OSX_EINVAL (-1)      /* bad argument: null pointer, negative size, Hq % Hkv != 0, overlap, a softmax over
+                                nothing (seq_k == 0 with query rows, cols == 0 with rows) */
 #define OSX_EUNSUPPORTED (-2) /* valid request outside what the kernels implement (head_dim, causal with Sq != Sk,
                                  one head's Q/K/V of 2^31 bytes or more) */
 #define OSX_EHIP (-3)        /* the HIP runtime reported an error at launch */
@@ -130,7 +132,8 @@ size_t osx_attn_fwd_workspace_bytes(int dtype, int batch, int heads_q, int heads
  * q, k, v, o: device pointers in the layouts above, all of element type
  * `dtype` (OSX_F32 or OSX_BF16); o is written in full.  scale <= 0 selects
  * 1/sqrt(head_dim) (page "softmax_attention": scores are multiplied by
- * d^-0.5).  workspace: device buffer of at least the bytes
+ * d^-0.5); a NaN or +inf scale, or one so large that scale * log2(e)
+ * overflows fp32, is OSX_EINVAL.  workspace: device buffer of at least the bytes
  * osx_attn_fwd_workspace reports (may be NULL when that is 0); its contents
  * on entry do not matter.  o must not overlap q, k, v or the workspace, nor
  * the workspace q, k or v (OSX_EINVAL).

@@ -186,6 +186,17 @@ int plan_softmax(int64_t rows, int64_t cols, osx_plan* p) {
 // True when p is not a multiple of `align` bytes.
 bool misaligned(const void* p, uintptr_t align) { return (reinterpret_cast<uintptr_t>(p) & (align - 1)) != 0; }
 
+// The attention scale: scale <= 0 selects 1/sqrt(head_dim); NaN, +inf, or a
+// scale so large that scale * log2(e) (the factor the kernels apply) is not a
+// finite fp32 value, is rejected.
+int attn_scale(float scale, int head_dim, float* out) {
+  if (std::isnan(scale) || (scale > 0.0f && !std::isfinite((float)((double)scale * 1.4426950408889634))))
+    return fail(OSX_EINVAL, "scale %g: must be finite with scale * log2(e) finite in fp32 (<= 0 selects 1/sqrt(d))",
+                (double)scale);
+  *out = scale > 0.0f ? scale : 1.0f / std::sqrt((float)head_dim);
+  return OSX_OK;
+}
+
 bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   const char* pa = (const char*)a;
   const char* pb = (const char*)b;
@@ -267,7 +278,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, b
     return fail(OSX_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : (size_t)0,
                 p.workspace_bytes);
   if (p.workspace_bytes > 0 && misaligned(workspace, 16)) return fail(OSX_EINVAL, "workspace must be 16-byte aligned");
-  if (!(scale > 0.0f) || !std::isfinite(scale)) scale = 1.0f / std::sqrt((float)head_dim);
+  if ((st = attn_scale(scale, head_dim, &scale)) != OSX_OK) return st;
   if (log_enabled()) {
     char shape[160];
     std::snprintf(shape, sizeof shape, "%s B=%d Hq=%d Hkv=%d Sq=%d Sk=%d d=%d causal=%d%s%s",
@@ -516,7 +527,7 @@ int osx_attn_fwd_unfused(const void* q, const void* k, const void* v, void* o, i
   if (!workspace || workspace_bytes < need)
     return fail(OSX_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : (size_t)0,
                 need);
-  if (!(scale > 0.0f) || !std::isfinite(scale)) scale = 1.0f / std::sqrt((float)head_dim);
+  if ((st = attn_scale(scale, head_dim, &scale)) != OSX_OK) return st;
   const size_t nq = (size_t)batch * heads_q * seq_q * head_dim * 2;
   const size_t nkv = (size_t)batch * heads_kv * seq_k * head_dim * 2;
   if (overlap(o, nq, q, nq) || overlap(o, nq, k, nkv) || overlap(o, nq, v, nkv) || overlap(o, nq, workspace, need))

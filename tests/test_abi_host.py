@@ -262,6 +262,26 @@ def test_non_finite_softmax_scale_is_rejected():
         assert "scale" in osx.last_error()
 
 
+def test_non_finite_attention_scale_is_rejected():
+    """scale <= 0 selects 1/sqrt(d); a NaN or +inf scale, or one whose log2(e) multiple overflows fp32, is an
+    error before anything is launched (not a silent fall back to the default)."""
+    lib = osx.lib
+    a, b, c, o = (ctypes.c_void_p(x) for x in (0x100000, 0x200000, 0x300000, 0x400000))
+    lse = ctypes.c_void_p(0x500000)
+    for bad in (float("nan"), float("inf"), 3.0e38):
+        for dtype in (F32, BF16):
+            assert lib.osx_attn_fwd(a, b, c, o, dtype, 1, 1, 1, 16, 16, 64, 0, bad, None, 0, None) == osx.OSX_EINVAL
+            assert "scale" in osx.last_error()
+            assert lib.osx_attn_fwd_lse(a, b, c, o, lse, dtype, 1, 1, 1, 16, 16, 64, 0, bad, None, 0,
+                                        None) == osx.OSX_EINVAL
+        assert lib.osx_attn_fwd_normalised(a, b, c, o, None, F32, 1, 1, 1, 16, 16, 64, 0, bad, None, 0,
+                                           None) == osx.OSX_EINVAL
+        need = osx.attn_fwd_unfused_workspace(BF16, 1, 4, 1, 128, 128, 64, True)
+        assert lib.osx_attn_fwd_unfused(a, b, c, o, BF16, 1, 4, 1, 128, 128, 64, 1, bad, ctypes.c_void_p(0x10000000),
+                                        need, None) == osx.OSX_EINVAL
+        assert "scale" in osx.last_error()
+
+
 @pytest.mark.parametrize("d", [16, 32, 48, 64, 80, 96, 112, 128])
 def test_bf16_head_dims_multiple_of_16_are_planned(d):
     """bf16 accepts every head_dim 16 k <= 128 (page "softmax_attention", section 实现思路, pads d up to the
