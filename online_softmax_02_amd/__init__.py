@@ -194,6 +194,8 @@ def _workspace(need: int, workspace, device):
         workspace = torch.empty(need, dtype=torch.uint8, device=device)
     if workspace is None:
         return None, None, 0
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor")
     return workspace, workspace.data_ptr(), workspace.numel() * workspace.element_size()
 
 
@@ -227,6 +229,8 @@ def _attn_prepare(q, k, v, causal, out, workspace, stream=None):
     squeeze = q.dim() == 2
     if squeeze:
         q, k, v = q[None, None], k[None, None], v[None, None]
+        if out is not None and out.dim() == 2:
+            out = out[None, None]
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D [B, H, S, D] (or 2-D [S, D])")
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -381,9 +385,11 @@ def attn_fwd_unfused(q, k, v, causal: bool = False, scale: float | None = None, 
     squeeze = q.dim() == 2
     if squeeze:
         q, k, v = q[None, None], k[None, None], v[None, None]
+        if out is not None and out.dim() == 2:
+            out = out[None, None]
     for name, t in (("q", q), ("k", k), ("v", v)):
         if t.dim() != 4 or not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous 4-D CUDA tensor")
+            raise ValueError(f"{name} must be a contiguous 4-D (or 2-D) CUDA tensor")
     if k.shape != v.shape or q.dtype != k.dtype or k.dtype != v.dtype:
         raise ValueError("k and v must match, and q, k, v share one dtype")
     B, Hq, Sq, D = q.shape

@@ -81,3 +81,30 @@ def test_tensors_on_a_device_that_is_not_current(osx):
     assert np.abs(y.cpu().numpy().astype(np.float64) - oracle.softmax_rows(x.cpu().numpy())).max() <= 1e-5
     with pytest.raises(ValueError, match="stream belongs"):
         osx.softmax_rows(x, stream=torch.cuda.Stream(device=0))
+
+
+def test_one_head_calls_take_a_2d_out(osx):
+    """q, k, v given as 2-D [S, D] (one head): every attention call accepts a 2-D ``out`` like q and writes it,
+    and returns 2-D results; the values match the oracle (fp32 bar)."""
+    t, q, k, v = _qkv(Sq=64, Sk=100, d=48)
+    q2, k2, v2 = q[0, 0].clone(), k[0, 0].clone(), v[0, 0].clone()  # head 0 as [S, D] (one KV head)
+    ref = oracle.attention(t["q"][:, :1], t["k"], t["v"])[0, 0]
+    for fn in (osx.attn_fwd, osx.attn_fwd_normalised):
+        out = torch.full_like(q2, float("nan"))
+        got = fn(q2, k2, v2, out=out)
+        assert got.shape == q2.shape and got.data_ptr() == out.data_ptr()
+        check(to_f64(out), ref, "f32", fn.__name__ + " 2-D out")
+        check(to_f64(fn(q2, k2, v2)), ref, "f32", fn.__name__ + " 2-D")
+    out = torch.full_like(q2, float("nan"))
+    osx.attn_fwd_noalloc(q2, k2, v2, out)
+    check(to_f64(out), ref, "f32", "noalloc 2-D out")
+    tb, qb, kb, vb = _qkv("bf16", Sq=64, Sk=100, d=64)
+    qb2, kb2, vb2 = qb[0, 0].clone(), kb[0, 0].clone(), vb[0, 0].clone()
+    refb = oracle.attention(tb["q"][:, :1], tb["k"], tb["v"])[0, 0]
+    out = torch.full_like(qb2, float("nan"))
+    got = osx.attn_fwd_unfused(qb2, kb2, vb2, out=out)
+    assert got.shape == qb2.shape and got.data_ptr() == out.data_ptr()
+    check(to_f64(out), refb, "bf16", "unfused 2-D out")
+    with pytest.raises(ValueError, match="contiguous"):
+        osx.attn_fwd(q, k, v, workspace=torch.empty(64, 64, dtype=torch.uint8, device="cuda")[:, ::2])
+
