@@ -9,6 +9,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <limits>
 #include <string>
 #include <thread>
 #include <vector>
@@ -112,6 +113,14 @@ static void attn_rejects() {
   EXPECT(osx_attn_fwd_lse(q, k, v, o, (float*)fake(0x400002), OSX_BF16, 1, 4, 1, 64, 64, 128, 0, 0.f, nullptr, 0,
                           nullptr) == OSX_EINVAL,
          "misaligned lse");
+  // a NaN, +inf or overflowing scale (scale * log2(e) past fp32) is rejected; <= 0 selects 1/sqrt(d)
+  for (float bad : {std::numeric_limits<float>::quiet_NaN(), std::numeric_limits<float>::infinity(), 3.0e38f}) {
+    EXPECT(osx_attn_fwd(q, k, v, o, OSX_BF16, 1, 4, 1, 64, 64, 128, 0, bad, nullptr, 0, nullptr) == OSX_EINVAL,
+           "scale %g", (double)bad);
+    EXPECT(osx_attn_fwd_normalised(q, k, v, o, nullptr, OSX_F32, 1, 1, 1, 64, 64, 64, 0, bad, nullptr, 0, nullptr) ==
+               OSX_EINVAL,
+           "normalised scale %g", (double)bad);
+  }
   // the normalised-output recurrence is fp32 only
   EXPECT(osx_attn_fwd_normalised(q, k, v, o, nullptr, OSX_BF16, 1, 4, 1, 64, 64, 128, 0, 0.f, nullptr, 0, nullptr) ==
              OSX_EUNSUPPORTED,
