@@ -143,7 +143,9 @@ int plan_attn(int dtype, int batch, int heads_q, int heads_kv, int seq_q, int se
     if (splits > 1) {
       p->splits = (int)splits;
       p->grid *= splits;
-      p->workspace_bytes = (size_t)((int64_t)batch * heads_q * seq_q * splits) * (size_t)(2 + head_dim) * sizeof(float);
+      // (m, l) pairs, then the accumulators from the next 16-byte boundary.
+      const int64_t parts = (int64_t)batch * heads_q * seq_q * splits;
+      p->workspace_bytes = (size_t)((parts * 2 + 3) / 4 * 4 + parts * head_dim) * sizeof(float);
     }
   }
   if (p->grid > 0x7fffffff) return fail(OSX_EUNSUPPORTED, "problem needs %lld workgroups", (long long)p->grid);

@@ -443,7 +443,8 @@ hipError_t launch(const AttnArgs& a) {
   const int kps = splits == 1 ? a.seq_k : ((a.seq_k + splits - 1) / splits + BN - 1) / BN * BN;
   const int64_t rows = (int64_t)a.batch * a.heads_q * a.seq_q;
   float* ws_ml = static_cast<float*>(a.workspace);
-  float* ws_acc = splits == 1 ? nullptr : ws_ml + rows * splits * 2;
+  // The slice accumulators start at the first 16-byte boundary after the (m, l) pairs.
+  float* ws_acc = splits == 1 ? nullptr : ws_ml + (rows * splits * 2 + 3) / 4 * 4;
   auto kernel = a.normalised ? prefill_f32_kernel<DP, true> : prefill_f32_kernel<DP, false>;
   hipLaunchKernelGGL(kernel, dim3((unsigned)a.plan.grid), dim3(kAttnThreads), 0, a.stream,
                      static_cast<const float*>(a.q), static_cast<const float*>(a.k), static_cast<const float*>(a.v),

@@ -335,6 +335,17 @@ def test_plans_beyond_any_device_are_rejected_without_overflow():
     assert osx.lib.osx_softmax_rows_workspace_bytes(2 ** 63 - 1, 2 ** 63 - 1) == 0
 
 
+def test_f32_split_accumulators_start_on_a_16_byte_boundary():
+    """The fp32 split workspace holds the (m, l) pairs of all partial states, then the accumulators from the next
+    16-byte boundary: with an odd number of partial states the pairs are padded by one pair."""
+    for shape, parts in [((1, 1, 1, 63, 1000, 48), 63 * 15), ((1, 1, 1, 1, 333, 128), 5),
+                         ((1, 1, 1, 4096, 4096, 128), 4096 * 16)]:
+        p = osx.attn_plan(F32, *shape)
+        assert p["splits"] * shape[3] == parts
+        d = shape[5]
+        assert p["workspace_bytes"] == (2 * parts + 2 * (parts % 2) + parts * d) * 4, (shape, p)
+
+
 def test_tensors_of_one_call_must_share_a_device():
     import torch
     with pytest.raises(ValueError, match="one CUDA device"):

@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_util import LSE_BF16_ATOL, check, to_dev, to_f64
+from tests.gpu_util import LSE_BF16_ATOL, LSE_F32_ATOL, check, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -151,6 +151,29 @@ def test_f32_long_sequence_sampled_rows(osx):
         fn(q, k, v, out=out)
         torch.cuda.synchronize()
         check(to_f64(out[0, 0, rows]), ref, "f32", f"long fp32 {fn.__name__}")
+
+
+@pytest.mark.parametrize("Sq,Sk,D", [(63, 1000, 48), (1, 333, 128), (127, 1990, 100)])
+def test_f32_split_with_an_odd_number_of_partial_states(osx, Sq, Sk, D):
+    """fp32 key split where rows x slices is odd, so the (m, l) pairs end off a 16-byte boundary and the slice
+    accumulators start at the next one: O and the log-sum-exp of the plain and the normalised-output forms
+    against the oracle."""
+    p = osx.attn_plan(osx.OSX_F32, 1, 1, 1, Sq, Sk, D)
+    parts = Sq * p["splits"]
+    assert p["splits"] > 1 and parts % 2 == 1, p
+    assert p["workspace_bytes"] == ((2 * parts + 3) // 4 * 4 + parts * D) * 4
+    print(f"case f32 odd partials Sq={Sq} Sk={Sk} d={D}", flush=True)
+    t = synth.random_attn(41, "f32", 1, 1, 1, Sq, Sk, D)
+    q, k, v = to_dev(t["q"]), to_dev(t["k"]), to_dev(t["v"])
+    ref_o = oracle.attention(t["q"], t["k"], t["v"])
+    ref_lse = oracle.attention_lse(t["q"], t["k"])
+    for fn in (osx.attn_fwd, osx.attn_fwd_normalised):
+        out = torch.full_like(q, float("nan"))
+        lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device="cuda")
+        fn(q, k, v, out=out, lse=lse)
+        torch.cuda.synchronize()
+        check(to_f64(out), ref_o, "f32", f"{fn.__name__} Sq={Sq} Sk={Sk}")
+        np.testing.assert_allclose(to_f64(lse), ref_lse, rtol=0, atol=LSE_F32_ATOL)
 
 
 def test_gqa_decode_bf16_full_size(osx):
